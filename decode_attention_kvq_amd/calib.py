@@ -1,0 +1,92 @@
+"""Host-side (offline) calibration of the per-KV-head key transform.
+
+Follows "WUSH-KV: KV Cache Quantization with Data-Adaptive Transforms":
+  §3    the transform comes from the second-order statistics of both factors of the
+        product: the Gram matrix M of the quantized tensor (the cached keys) and the
+        Hessian H of its partner; damping makes both positive definite; a scalar keeps
+        the Frobenius norm (exactly when undamped); rescaling M or H changes nothing.
+  §4.2  one key transform per KV head, with a local surrogate Hessian.  For keys the
+        partner is the query: a key error e moves the logit of query q by q.e, so
+        H = sum over the query heads that read the KV head of E[q^T q].
+  App. B.2  undamped, the transform minimises tr(T^T M T) tr(T^-1 H T^-T).
+
+The formula itself is not printed on the pages; this module uses the closed form that
+has every stated property (balanced: T^T M T and T^-1 H T^-T are both diagonal-equal):
+
+    M + g tr(M)/d I = B B^T,  H + g tr(H)/d I = A A^T     (Cholesky)
+    B^T A = U S V^T                                      (SVD)
+    T = c * B^-T U S^1/2 * Hd,  c^2 = tr(M)/tr(S)
+
+with each column of B^-T U S^1/2 signed so that its largest-magnitude entry is
+positive, and Hd the normalised Sylvester-Hadamard matrix, an orthogonal factor the
+unclipped loss does not see that equalises the transformed channels' variances for the
+per-token group clip.  Everything is fp64; the stored transform is rounded to bf16 and
+the query side uses the exact inverse-transpose of the rounded matrix.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+DEFAULT_GAMMA = 0.01
+
+
+def sylvester_hadamard(d: int) -> np.ndarray:
+    if d & (d - 1):
+        raise ValueError("d must be a power of two")
+    h = np.array([[1.0]])
+    while h.shape[0] < d:
+        h = np.kron(np.array([[1.0, 1.0], [1.0, -1.0]]), h)
+    return h / np.sqrt(d)
+
+
+def key_statistics(k_cal: np.ndarray, q_cal: np.ndarray):
+    """Gram matrix of the keys and the summed query second moment of one KV head.
+
+    k_cal: [N, d] post-RoPE keys; q_cal: [G, N_q, d] post-RoPE queries of the G query
+    heads that read this KV head."""
+    k = np.asarray(k_cal, dtype=np.float64)
+    q = np.asarray(q_cal, dtype=np.float64)
+    if q.ndim == 2:
+        q = q[None]
+    gram = np.einsum("nc,nd->cd", k, k) / k.shape[0]
+    hess = np.einsum("gnc,gnd->cd", q, q) / q.shape[1]
+    return gram, hess
+
+
+def wush(gram: np.ndarray, hess: np.ndarray, gamma: float = DEFAULT_GAMMA,
+         hadamard: bool = True) -> np.ndarray:
+    d = gram.shape[0]
+    eye = np.eye(d)
+    b = np.linalg.cholesky(gram + gamma * np.trace(gram) / d * eye)
+    a = np.linalg.cholesky(hess + gamma * np.trace(hess) / d * eye)
+    u, s, _ = np.linalg.svd(b.T @ a)
+    t0 = np.linalg.solve(b.T, u) * np.sqrt(s)
+    lead = np.abs(t0).argmax(axis=0)
+    t0 *= np.sign(t0[lead, np.arange(d)])
+    t = np.sqrt(np.trace(gram) / s.sum()) * t0
+    return t @ sylvester_hadamard(d) if hadamard else t
+
+
+def round_bf16(x: np.ndarray) -> np.ndarray:
+    """fp64 -> bf16 (round to nearest even, directly from fp64), as fp32 values."""
+    x = np.asarray(x, dtype=np.float64)
+    m, e = np.frexp(x)                       # x = m 2^e, |m| in [0.5, 1)
+    return (np.round(m * 256.0) / 256.0 * np.exp2(e)).astype(np.float32)
+
+
+def calibrate_key_transform(k_cal: np.ndarray, q_cal: np.ndarray, gamma: float = DEFAULT_GAMMA,
+                            hadamard: bool = True, store_bf16: bool = True):
+    """Returns (T, T_inv_T) for one KV head as fp32 arrays [d, d].
+
+    T is what the write path applies (k' = k T); when store_bf16 it holds bf16 values.
+    T_inv_T = (T^-1)^T of exactly that stored T, for the read path (q' = q T^-T)."""
+    t = wush(*key_statistics(k_cal, q_cal), gamma=gamma, hadamard=hadamard)
+    t_store = round_bf16(t) if store_bf16 else t.astype(np.float32)
+    t_inv_t = np.linalg.inv(t_store.astype(np.float64)).T.astype(np.float32)
+    return t_store, t_inv_t
+
+
+def calibrate_all_heads(k_cal_heads, q_cal_heads, **kw):
+    """Stacks calibrate_key_transform over KV heads: returns ([H,d,d], [H,d,d])."""
+    pairs = [calibrate_key_transform(k, q, **kw) for k, q in zip(k_cal_heads, q_cal_heads)]
+    return np.stack([p[0] for p in pairs]), np.stack([p[1] for p in pairs])

@@ -1,0 +1,154 @@
+"""Pins of the oracle's transform, clip bounds and affine codes (O1-O4).
+
+Each check ties the oracle to something other than itself: numpy's percentile routine,
+a brute-force sort, the RMS closed form, an fp64 matmul, the half-step error bound of
+uniform rounding and a brute-force nearest-level search."""
+import numpy as np
+import pytest
+
+from decode_attention_kvq_amd import synth
+
+
+def _ulp(x):
+    return np.spacing(np.abs(np.asarray(x, np.float32)))
+
+
+def _rows(n, seed, scale=1.0):
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal((n, 128)).astype(np.float32) * np.float32(scale)
+    # heavy-tailed rows, repeated values, exact zeros of both signs
+    x[1::7] = (rng.standard_t(2, size=(len(x[1::7]), 128))).astype(np.float32)
+    x[2::11, :64] = 0.0
+    x[2::11, 64:70] = -0.0
+    x[3::13] = np.round(x[3::13])
+    return x
+
+
+def test_percentile_positions_worked_values(orc):
+    # rank = p*(n-1): 0.01*127 = 1.27 and 0.99*127 = 125.73
+    i, f = orc.percentile_position(0.01)
+    assert i == 1 and f == np.float32(0.27)
+    i, f = orc.percentile_position(0.99)
+    assert i == 125 and f == np.float32(0.73)
+    assert orc.percentile_position(0.0) == (0, 0.0)
+    assert orc.percentile_position(1.0) == (127, 0.0)
+    assert orc.percentile_position(0.5) == (63, 0.5)
+
+
+@pytest.mark.parametrize("p_lo,p_hi", [(0.01, 0.99), (0.0, 1.0), (0.05, 0.9), (0.25, 0.75)])
+def test_percentile_matches_numpy(orc, p_lo, p_hi):
+    x = _rows(2000, 7)
+    _, _, _, lo, hi = orc.quantize_rows(x, 2, orc.PERCENTILE, p_lo, p_hi)
+    ref = np.percentile(x.astype(np.float64), [100 * p_lo, 100 * p_hi], axis=1, method="linear")
+    for got, r in ((lo, ref[0]), (hi, ref[1])):
+        tol = 2 * _ulp(r) + 1e-30
+        assert np.all(np.abs(got - r) <= tol), np.max(np.abs(got - r) / tol)
+
+
+def test_percentile_order_statistics_brute_force(orc):
+    x = _rows(500, 8)
+    _, _, _, lo, hi = orc.quantize_rows(x, 4, orc.PERCENTILE, 0.0, 1.0)
+    assert np.array_equal(lo, x.min(axis=1) + np.float32(0))
+    assert np.array_equal(hi, x.max(axis=1) + np.float32(0))
+    # p such that the rank is an integer: exactly the order statistic
+    s = np.sort(x, axis=1)
+    _, _, _, lo, hi = orc.quantize_rows(x, 4, orc.PERCENTILE, 2 / 127, 124 / 127)
+    assert np.array_equal(lo, s[:, 2] + np.float32(0))
+    assert np.array_equal(hi, s[:, 124] + np.float32(0))
+
+
+def test_rms_clip_closed_form(orc):
+    x = _rows(2000, 9)
+    alpha = 2.83
+    _, _, _, lo, hi = orc.quantize_rows(x, 2, orc.RMS, alpha=alpha)
+    ref = alpha * np.sqrt(np.mean(x.astype(np.float64) ** 2, axis=1))
+    assert np.all(np.abs(hi - ref) <= 4 * _ulp(ref) + 1e-30)
+    assert np.array_equal(lo, -hi)
+
+
+@pytest.mark.parametrize("bits", [2, 3, 4])
+@pytest.mark.parametrize("quant", [0, 1])
+def test_codes_range_error_bound_and_nearest_level(orc, bits, quant):
+    x = _rows(3000, 10 + bits)
+    codes, s16, z16, lo, hi = orc.quantize_rows(x, bits, quant, 0.01, 0.99, 2.83)
+    L = (1 << bits) - 1
+    assert codes.max() <= L
+    s = s16.view(np.float16).astype(np.float64)[:, None]
+    z = z16.view(np.float16).astype(np.float64)[:, None]
+    # stored scale/zero are the fp16 roundings of (hi-lo)/L and lo
+    assert np.array_equal(s16, np.clip((hi - lo) / np.float32(L), -65504, 65504).astype(np.float16).view(np.uint16))
+    assert np.array_equal(z16, np.clip(lo, -65504, 65504).astype(np.float16).view(np.uint16))
+    xd = x.astype(np.float64)
+    xhat = codes * s + z
+    inside = (xd >= z - s / 2) & (xd <= z + (L + 0.5) * s) & (s > 0)
+    err = np.abs(xd - xhat)
+    slack = 4 * np.spacing(np.maximum(np.abs(xd), np.abs(z)).astype(np.float32)) + 1e-30
+    bound = np.broadcast_to(s / 2, err.shape) + slack
+    assert np.all(err[inside] <= bound[inside])
+    # brute-force nearest level (fp64) for every element away from a decision boundary
+    levels = z[:, :, None] + s[:, :, None] * np.arange(L + 1)[None, None, :]
+    d = np.abs(xd[:, :, None] - levels)
+    best = np.argmin(d, axis=2)
+    srt = np.sort(d, axis=2)
+    clear = (srt[:, :, 1] - srt[:, :, 0]) > 1e-5 * np.maximum(s, 1e-30)
+    assert np.array_equal(codes[clear], best[clear])
+    # clipped elements go to the end codes
+    assert np.all(codes[(xd < z - s) & (s > 0)] == 0)
+    assert np.all(codes[(xd > z + (L + 1) * s) & (s > 0)] == L)
+
+
+def test_degenerate_group(orc):
+    x = np.full((3, 128), 0.3, np.float32)
+    x[1] = 0.0
+    x[2] = -70000.0
+    codes, s16, z16, _, _ = orc.quantize_rows(x, 2, orc.PERCENTILE)
+    assert codes.max() == 0
+    assert np.all(s16 == 0)
+    assert z16[0] == np.float16(0.3).view(np.uint16)
+    assert z16[2] == np.float16(-65504).view(np.uint16)     # saturated, not -inf
+
+
+def test_transform_matches_fp64_matmul(orc):
+    rng = np.random.default_rng(3)
+    k = synth.bf16_round(rng.standard_normal((40, 3, 128)).astype(np.float32))
+    t = synth.bf16_round(rng.standard_normal((3, 128, 128)).astype(np.float32) * 0.1)
+    got = orc.transform_keys(k, t)
+    ref = np.einsum("nhc,hcj->nhj", k.astype(np.float64), t.astype(np.float64))
+    assert np.all(np.abs(got - ref) <= 0.5 * _ulp(ref) + 1e-30)
+    assert np.array_equal(orc.transform_keys(k, None), k)
+
+
+def test_query_compensation_identity(orc):
+    """(q T^-T).(k T) == q.k: the key transform is invisible to the logits once the
+    query is compensated (WUSH-KV summary, §4.2), also for a bf16-rounded T paired with
+    the exact inverse of the rounded matrix."""
+    from oracle import wush
+    rng = np.random.default_rng(4)
+    k = rng.standard_normal((64, 1, 128))
+    q = rng.standard_normal((5, 128))
+    t = rng.standard_normal((128, 128)) / np.sqrt(128) + np.eye(128)
+    for tt in (t, wush.bf16_round(t).astype(np.float64)):
+        tinv_t = np.linalg.inv(tt).T
+        kp = np.einsum("nc,cj->nj", k[:, 0], tt)
+        qp = q @ tinv_t
+        assert np.allclose(qp @ kp.T, q @ k[:, 0].T, rtol=0, atol=1e-10)
+    # the oracle's fp32-rounded transform keeps the identity to fp32 accuracy
+    tb = wush.bf16_round(t)
+    kp32 = orc.transform_keys(k.astype(np.float32), tb[None])[:, 0].astype(np.float64)
+    qp = q @ np.linalg.inv(tb.astype(np.float64)).T
+    ref = q @ k[:, 0].T
+    assert np.max(np.abs(qp @ kp32.T - ref)) < 1e-4 * np.max(np.abs(ref))
+
+
+def test_identity_transform_reduces_to_plain_quantizer(orc):
+    w = synth.WORKLOADS["tiny"]
+    k, v = synth.kv_tokens(w, 256)
+    slots = np.arange(256, dtype=np.int64)
+    pools = []
+    for t in (None, np.eye(128, dtype=np.float32)[None]):
+        kp = orc.new_pool(4, 1, 4)
+        vp = orc.new_pool(4, 1, 4)
+        orc.append(kp, vp, k, v, slots, t_k=t, bits_k=4, bits_v=4)
+        pools.append((kp, vp))
+    assert np.array_equal(pools[0][0], pools[1][0])
+    assert np.array_equal(pools[0][1], pools[1][1])
