@@ -1,0 +1,228 @@
+"""Benchmark of one decode step of the quantized-KV-cache hot path on one MI355X.
+
+A step is the whole hot path over one batch: kvq_quantize_append of the batch's new
+tokens (one per sequence, dense key transform on the matrix cores, 2-bit percentile
+codes) followed by kvq_decode_attn over every cached token.  Default workload: the
+Qwen3-8B-shaped layer (32 query heads, 8 KV heads, head_dim 128) at batch 64 x 16384
+cached tokens, 2-bit K and V, synthetic Sigma-model data, caches resident in HBM.
+
+Prints one JSON line.  `value` is cached tokens read per second (batch x context per
+step time).  `roofline` is for the decode kernel: algorithmic bytes per launch over its
+average launch time (HIP events on the launch stream) against 8 TB/s.  `cpu_baseline`
+is the CPU oracle's decode timed on a bounded sample of sequences of the same shape.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK = 8.0e12
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="qwen3-8b-b64-16k")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--extra", action="store_true", help="also time the other workloads")
+    return ap.parse_args()
+
+
+def decode_algorithmic_bytes(w, B, seq_len) -> int:
+    """Bytes the decode step must move: packed K and V of every cached token (codes +
+    fp16 scale and zero), the queries (bf16), the output (fp32), the block table (int32
+    per page) and the inverse-transpose transform (fp32, 64 KiB per KV head)."""
+    per_token = w.heads_kv * ((128 * w.bits_k // 8 + 4) + (128 * w.bits_v // 8 + 4))
+    pages = -(-seq_len // 64)
+    return (B * seq_len * per_token + B * w.heads_q * 128 * 2 + B * w.heads_q * 128 * 4
+            + B * pages * 4 + w.heads_kv * 128 * 128 * 4)
+
+
+def append_algorithmic_bytes(w, n) -> int:
+    """k and v in (bf16), T (bf16), slots (int64), codes and metadata out."""
+    per = w.heads_kv * 128 * 2 * 2 + 8
+    out = w.heads_kv * ((128 * w.bits_k // 8 + 4) + (128 * w.bits_v // 8 + 4))
+    return n * (per + out) + w.heads_kv * 128 * 128 * 2
+
+
+def setup_decode(w, torch, api, calib, synth, dev):
+    B, H, pps = w.batch, w.heads_kv, w.pages_per_seq
+    cache = api.KVCache(B * pps, H, w.bits_k, w.bits_v, w.quantizer, w.quantizer, w.p_lo, w.p_hi,
+                        w.alpha, w.alpha, device=dev)
+    ts, tis = [], []
+    for h in range(H):
+        kc, qc = synth.calibration_set(w.config, h, w.group)
+        t, ti = calib.calibrate_key_transform(kc, qc)
+        ts.append(t)
+        tis.append(ti)
+    t_k = torch.from_numpy(np.stack(ts)).to(torch.bfloat16).to(dev)
+    t_inv = torch.from_numpy(np.stack(tis)).to(dev)
+    # fill the cache sequence by sequence with the GPU write path
+    per = max(1, (1 << 21) // w.seq_len)
+    for b0 in range(0, B, per):
+        nb = min(per, B - b0)
+        k, v = synth.kv_tokens_torch(w, nb * w.seq_len, dev, seq=b0)
+        slots = torch.arange(b0 * pps * 64, b0 * pps * 64 + nb * w.seq_len, dtype=torch.int64, device=dev)
+        api.kvq_quantize_append(cache, k, v, slots, t_k=t_k)
+        del k, v
+    torch.cuda.synchronize()
+    bt = torch.from_numpy(synth.contiguous_block_table(B, pps)).to(dev)
+    seq = torch.full((B,), w.seq_len, dtype=torch.int32, device=dev)
+    q = torch.from_numpy(synth.decode_queries(w)).to(torch.bfloat16).to(dev)
+    # the step's new token of each sequence is appended at its last position
+    knew, vnew = synth.kv_tokens_torch(w, B, dev, seq=10_000)
+    new_slots = torch.tensor([b * pps * 64 + w.seq_len - 1 for b in range(B)], dtype=torch.int64, device=dev)
+    ws = torch.empty(max(1, api.decode_workspace_bytes(cache, B, w.heads_q, w.seq_len)), dtype=torch.uint8,
+                     device=dev)
+    out = torch.empty((B, w.heads_q, 128), dtype=torch.float32, device=dev)
+    return dict(cache=cache, t_k=t_k, t_inv=t_inv, bt=bt, seq=seq, q=q, knew=knew, vnew=vnew,
+                new_slots=new_slots, ws=ws, out=out)
+
+
+def time_steps(w, s, torch, api, steps, warmup):
+    def step(ev=None):
+        if ev:
+            ev[0].record()
+        api.kvq_quantize_append(s["cache"], s["knew"], s["vnew"], s["new_slots"], t_k=s["t_k"])
+        if ev:
+            ev[1].record()
+        api.kvq_decode_attn(s["cache"], s["q"], s["bt"], s["seq"], w.seq_len, t_k_inv_t=s["t_inv"],
+                            out=s["out"], workspace=s["ws"])
+        if ev:
+            ev[2].record()
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    t0 = time.perf_counter()
+    for i in range(steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    app = [e[0].elapsed_time(e[1]) for e in evs]
+    dec = [e[1].elapsed_time(e[2]) for e in evs]
+    return wall / steps * 1e3, float(np.mean(app)), float(np.mean(dec)), float(np.median(dec))
+
+
+def time_prefill(w, torch, api, calib, synth, dev, reps=20):
+    n, H = w.seq_len, w.heads_kv
+    cache = api.KVCache(n // 64, H, w.bits_k, w.bits_v, device=dev)
+    k, v = synth.kv_tokens_torch(w, n, dev)
+    ts = [calib.calibrate_key_transform(*synth.calibration_set(w.config, h, 4))[0] for h in range(H)]
+    t_k = torch.from_numpy(np.stack(ts)).to(torch.bfloat16).to(dev)
+    slots = torch.arange(n, dtype=torch.int64, device=dev)
+    for _ in range(3):
+        api.kvq_quantize_append(cache, k, v, slots, t_k=t_k)
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    ev[0].record()
+    for _ in range(reps):
+        api.kvq_quantize_append(cache, k, v, slots, t_k=t_k)
+    ev[1].record()
+    torch.cuda.synchronize()
+    ms = ev[0].elapsed_time(ev[1]) / reps
+    by = append_algorithmic_bytes(w, n)
+    return {"workload": w.name, "us": ms * 1e3, "GB_s": by / (ms * 1e-3) / 1e9,
+            "frac": by / (ms * 1e-3) / HBM_PEAK, "algorithmic_bytes": by}
+
+
+def cpu_baseline(w, seconds):
+    """The oracle's decode attention on whole sequences of the workload's shape (random
+    packed codes: the oracle's cost does not depend on the values), single thread."""
+    import oracle
+    from decode_attention_kvq_amd import synth
+    rng = np.random.default_rng(0)
+    H, pps = w.heads_kv, w.pages_per_seq
+    kp = synth.random_packed_pool(rng, pps, H, w.bits_k)
+    vp = synth.random_packed_pool(rng, pps, H, w.bits_v)
+    bt = np.arange(pps, dtype=np.int32)[None]
+    seq = np.array([w.seq_len], np.int32)
+    q = synth.decode_queries(w, batch=1)
+    tinv = np.broadcast_to(np.eye(128, dtype=np.float32), (H, 128, 128)).copy()
+    done, t0 = 0, time.perf_counter()
+    while True:
+        oracle.decode_attention(kp, vp, q, bt, seq, t_inv_t=tinv, bits_k=w.bits_k, bits_v=w.bits_v)
+        done += 1
+        el = time.perf_counter() - t0
+        if el >= seconds or done >= 64:
+            break
+    return {"value": done * w.seq_len / el, "unit": "cached tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"{done} sequence(s) of {w.seq_len} tokens x {w.heads_q} query heads "
+                      f"(one decode step each), single thread, {el:.1f} s"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the decode path would shard by KV head with no exchange)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    from decode_attention_kvq_amd import api, calib, synth
+    from decode_attention_kvq_amd import build as kbuild
+    if not os.path.exists(os.path.join(ROOT, "decode_attention_kvq_amd", "libkvq.so")):
+        kbuild.build()
+    dev = torch.device("cuda:0")
+    w = synth.WORKLOADS[args.workload]
+    s = setup_decode(w, torch, api, calib, synth, dev)
+    ms_step, ms_app, ms_dec, ms_dec_med = time_steps(w, s, torch, api, args.steps, args.warmup)
+    cached = w.batch * w.seq_len
+    dbytes = decode_algorithmic_bytes(w, w.batch, w.seq_len)
+    achieved = dbytes / (ms_dec * 1e-3)
+    rec = {
+        "metric": "decode-attn cached tokens/s + HBM GB/s (% of peak), 2-bit, batch x 16K ctx",
+        "value": cached / (ms_step * 1e-3),
+        "unit": "cached tokens/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "u2 codes, f16 matrix-core products, f32 accumulate",
+        "data": "synthetic",
+        "config": {"workload": w.name, "batch": w.batch, "seq_len": w.seq_len, "heads_q": w.heads_q,
+                   "heads_kv": w.heads_kv, "head_dim": 128, "bits_k": w.bits_k, "bits_v": w.bits_v,
+                   "quantizer": w.quantizer, "page_tokens": 64, "parallelism": "single GPU"},
+        "roofline": {"bound": "hbm", "achieved": achieved / 1e9, "peak": HBM_PEAK / 1e9, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK, "traffic": None,
+                     "kernel": "kvq decode (main + split combine)", "algorithmic_bytes": dbytes,
+                     "avg_us": ms_dec * 1e3, "median_us": ms_dec_med * 1e3},
+        "append_us": ms_app * 1e3,
+        "decode_GB_s": achieved / 1e9,
+        "decode_tokens_per_s": cached / (ms_dec * 1e-3),
+    }
+    del s
+    torch.cuda.empty_cache()
+    if args.extra:
+        extra = {}
+        for name in ("qwen3-8b-b1-16k", "long-b16-128k-quest"):
+            w2 = synth.WORKLOADS[name]
+            s2 = setup_decode(w2, torch, api, calib, synth, dev)
+            _, _, md, _ = time_steps(w2, s2, torch, api, 20, 5)
+            by = decode_algorithmic_bytes(w2, w2.batch, w2.seq_len)
+            extra[name] = {"decode_us": md * 1e3, "GB_s": by / (md * 1e-3) / 1e9,
+                           "frac": by / (md * 1e-3) / HBM_PEAK,
+                           "tokens_per_s": w2.batch * w2.seq_len / (md * 1e-3)}
+            del s2
+            torch.cuda.empty_cache()
+        for name in ("prefill-8x32k-4bit", "prefill-8x32k-2bit"):
+            extra[name] = time_prefill(synth.WORKLOADS[name], torch, api, calib, synth, dev)
+        rec["other_workloads"] = extra
+    if not args.no_cpu_baseline:
+        rec["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,129 @@
+"""Python binding of the kvq C ABI for torch tensors.
+
+Argument marshalling only: tensors supply device pointers, the current torch stream
+supplies the hipStream_t, and every step of the computation runs in the HIP kernels of
+libkvq.so.  Function names follow the C entry points (kvq_quantize_append,
+kvq_decode_attn, kvq_dequant).
+"""
+from __future__ import annotations
+
+import ctypes as C
+import math
+
+import torch
+
+from ._lib import KvqCacheDesc, check, load
+
+HEAD_DIM = 128
+PAGE_TOKENS = 64
+QUANTIZERS = {"percentile": 0, "rms": 1}
+_DTYPES = {torch.float32: 0, torch.bfloat16: 1, torch.float16: 2}
+
+
+def block_bytes(bits: int) -> int:
+    n = int(load().kvq_block_bytes(bits))
+    if n == 0:
+        raise ValueError("bits must be 2 or 4")
+    return n
+
+
+def _ptr(t):
+    return None if t is None else C.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return C.c_void_p(s.cuda_stream)
+
+
+def _dev(t, name, dtype=None):
+    if t is None:
+        return
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}")
+
+
+class KVCache:
+    """One layer's paged, packed K and V pools ([num_pages, kv_heads, block_bytes] uint8)."""
+
+    def __init__(self, num_pages: int, num_kv_heads: int, bits_k: int = 2, bits_v: int = 2,
+                 quant_k: str = "percentile", quant_v: str = "percentile", p_lo: float = 0.01,
+                 p_hi: float = 0.99, alpha_k: float = 2.83, alpha_v: float = 2.83,
+                 device="cuda", k_pages=None, v_pages=None):
+        self.num_pages, self.num_kv_heads = num_pages, num_kv_heads
+        self.bits_k, self.bits_v = bits_k, bits_v
+        self.quant_k, self.quant_v = quant_k, quant_v
+        self.p_lo, self.p_hi, self.alpha_k, self.alpha_v = p_lo, p_hi, alpha_k, alpha_v
+        shape_k = (num_pages, num_kv_heads, block_bytes(bits_k))
+        shape_v = (num_pages, num_kv_heads, block_bytes(bits_v))
+        self.k_pages = torch.zeros(shape_k, dtype=torch.uint8, device=device) if k_pages is None else k_pages
+        self.v_pages = torch.zeros(shape_v, dtype=torch.uint8, device=device) if v_pages is None else v_pages
+        assert tuple(self.k_pages.shape) == shape_k and tuple(self.v_pages.shape) == shape_v
+        _dev(self.k_pages, "k_pages", torch.uint8)
+        _dev(self.v_pages, "v_pages", torch.uint8)
+
+    def desc(self) -> KvqCacheDesc:
+        return KvqCacheDesc(self.num_kv_heads, HEAD_DIM, PAGE_TOKENS, self.bits_k, self.bits_v,
+                            QUANTIZERS[self.quant_k], QUANTIZERS[self.quant_v], self.p_lo, self.p_hi,
+                            self.alpha_k, self.alpha_v, self.num_pages, self.k_pages.data_ptr(),
+                            self.v_pages.data_ptr())
+
+
+def kvq_quantize_append(cache: KVCache, k: torch.Tensor, v: torch.Tensor, slot_mapping: torch.Tensor,
+                        t_k: torch.Tensor | None = None, stream=None) -> None:
+    """k, v: [n, kv_heads, 128] (f32/bf16/f16); slot_mapping: [n] int64; t_k: [kv_heads,128,128]."""
+    _dev(k, "k"); _dev(v, "v", k.dtype); _dev(slot_mapping, "slot_mapping", torch.int64)
+    _dev(t_k, "t_k", k.dtype)
+    n = k.shape[0]
+    assert k.shape == (n, cache.num_kv_heads, HEAD_DIM) and v.shape == k.shape
+    assert slot_mapping.shape == (n,)
+    d = cache.desc()
+    check(load().kvq_quantize_append(C.byref(d), _ptr(k), _ptr(v), _DTYPES[k.dtype], n,
+                                     _ptr(slot_mapping), _ptr(t_k), _DTYPES[k.dtype], _stream(stream)))
+
+
+def decode_workspace_bytes(cache: KVCache, batch: int, num_q_heads: int, max_seq_len: int) -> int:
+    d = cache.desc()
+    return int(load().kvq_decode_workspace_bytes(C.byref(d), batch, num_q_heads, max_seq_len))
+
+
+def kvq_decode_attn(cache: KVCache, q: torch.Tensor, block_table: torch.Tensor, seq_lens: torch.Tensor,
+                    max_seq_len: int, t_k_inv_t: torch.Tensor | None = None, sm_scale: float | None = None,
+                    out: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
+                    stream=None) -> torch.Tensor:
+    """q: [B, Hq, 128]; block_table: [B, max_pages] int32; seq_lens: [B] int32.
+    Returns out [B, Hq, 128] fp32 in the transformed value basis."""
+    _dev(q, "q"); _dev(block_table, "block_table", torch.int32); _dev(seq_lens, "seq_lens", torch.int32)
+    _dev(t_k_inv_t, "t_k_inv_t", torch.float32)
+    B, Hq, _ = q.shape
+    if out is None:
+        out = torch.empty((B, Hq, HEAD_DIM), dtype=torch.float32, device=q.device)
+    _dev(out, "out", torch.float32)
+    if sm_scale is None:
+        sm_scale = 1.0 / math.sqrt(HEAD_DIM)
+    need = decode_workspace_bytes(cache, B, Hq, max_seq_len)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    d = cache.desc()
+    check(load().kvq_decode_attn(C.byref(d), _ptr(q), _DTYPES[q.dtype], B, Hq, _ptr(t_k_inv_t),
+                                 _ptr(block_table), block_table.shape[1], _ptr(seq_lens), max_seq_len,
+                                 float(sm_scale), _ptr(out), _ptr(workspace), ws_bytes, _stream(stream)))
+    return out
+
+
+def kvq_dequant(cache: KVCache, which: int, slots: torch.Tensor, out: torch.Tensor | None = None,
+                stream=None) -> torch.Tensor:
+    """which = 0 keys, 1 values; slots: [n] int64 -> [n, kv_heads, 128] fp32."""
+    _dev(slots, "slots", torch.int64)
+    n = slots.shape[0]
+    if out is None:
+        out = torch.zeros((n, cache.num_kv_heads, HEAD_DIM), dtype=torch.float32, device=slots.device)
+    _dev(out, "out", torch.float32)
+    d = cache.desc()
+    check(load().kvq_dequant(C.byref(d), which, _ptr(slots), n, _ptr(out), _stream(stream)))
+    return out

@@ -1,0 +1,195 @@
+// C ABI of the kvq library: host-side validation, then kernel dispatch on the caller's
+// stream.  Nothing here allocates or synchronises.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdio>
+#include <string>
+
+#include "../../include/kvq.h"
+#include "kvq_internal.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+kvq_status fail(kvq_status s, const char* msg) {
+  g_last_error = msg;
+  return s;
+}
+
+kvq_status check_cache(const kvq_cache_desc* c, bool need_k, bool need_v) {
+  if (!c) return fail(KVQ_ERR_INVALID_ARG, "cache descriptor is null");
+  if (c->head_dim != 128) return fail(KVQ_ERR_UNSUPPORTED, "head_dim must be 128");
+  if (c->page_size != 64) return fail(KVQ_ERR_UNSUPPORTED, "page_size must be 64");
+  if (c->num_kv_heads < 1) return fail(KVQ_ERR_INVALID_ARG, "num_kv_heads must be >= 1");
+  if (c->num_kv_heads > 65535) return fail(KVQ_ERR_UNSUPPORTED, "num_kv_heads must be <= 65535");
+  if ((c->bits_k != 2 && c->bits_k != 4) || (c->bits_v != 2 && c->bits_v != 4))
+    return fail(KVQ_ERR_UNSUPPORTED, "bits_k and bits_v must be 2 or 4");
+  if (c->num_pages < 0) return fail(KVQ_ERR_INVALID_ARG, "num_pages must be >= 0");
+  if (need_k && !c->k_pages) return fail(KVQ_ERR_INVALID_ARG, "k_pages is null");
+  if (need_v && !c->v_pages) return fail(KVQ_ERR_INVALID_ARG, "v_pages is null");
+  return KVQ_OK;
+}
+
+kvq_status check_quantizer(int q, float alpha, float p_lo, float p_hi) {
+  if (q == KVQ_Q_PERCENTILE) {
+    if (!(std::isfinite(p_lo) && std::isfinite(p_hi) && p_lo >= 0.0f && p_lo <= p_hi && p_hi <= 1.0f))
+      return fail(KVQ_ERR_INVALID_ARG, "percentiles must satisfy 0 <= p_lo <= p_hi <= 1");
+    return KVQ_OK;
+  }
+  if (q == KVQ_Q_RMS) {
+    if (!(std::isfinite(alpha) && alpha > 0.0f)) return fail(KVQ_ERR_INVALID_ARG, "alpha must be > 0");
+    return KVQ_OK;
+  }
+  return fail(KVQ_ERR_INVALID_ARG, "unknown quantizer");
+}
+
+// Linear-interpolation percentile position over 128 sorted values.
+void percentile_position(float p, int* i, float* f) {
+  const double rank = (double)p * 127.0;
+  int ii = (int)std::floor(rank);
+  if (ii < 0) ii = 0;
+  float ff = (float)(rank - (double)ii);
+  if (ii >= 127) { ii = 127; ff = 0.0f; }
+  *i = ii;
+  *f = ff;
+}
+
+bool valid_dtype(int d) { return d == KVQ_F32 || d == KVQ_BF16 || d == KVQ_F16; }
+
+kvq_status hip_status(hipError_t e) {
+  if (e == hipSuccess) return KVQ_OK;
+  g_last_error = std::string("HIP error: ") + hipGetErrorString(e);
+  return KVQ_ERR_HIP;
+}
+
+struct WorkspaceLayout {
+  size_t o_bytes, ml_bytes, total;
+};
+
+WorkspaceLayout workspace_layout(int batch, int heads_q, int chunks) {
+  WorkspaceLayout w{0, 0, 0};
+  if (chunks <= 1 || batch <= 0) return w;
+  const size_t rows = (size_t)batch * heads_q * chunks;
+  w.o_bytes = (rows * 128 * sizeof(float) + 255) & ~(size_t)255;
+  w.ml_bytes = (rows * 2 * sizeof(float) + 255) & ~(size_t)255;
+  w.total = w.o_bytes + w.ml_bytes;
+  return w;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t kvq_block_bytes(int32_t bits) {
+  if (bits != 2 && bits != 4) return 0;
+  return (size_t)(64 * 128 * bits / 8 + 4 * 64);
+}
+
+const char* kvq_status_string(kvq_status s) {
+  switch (s) {
+    case KVQ_OK: return "ok";
+    case KVQ_ERR_INVALID_ARG: return "invalid argument";
+    case KVQ_ERR_UNSUPPORTED: return "unsupported configuration";
+    case KVQ_ERR_WORKSPACE: return "workspace too small";
+    case KVQ_ERR_HIP: return "HIP error";
+  }
+  return "unknown status";
+}
+
+const char* kvq_last_error(void) { return g_last_error.c_str(); }
+
+kvq_status kvq_quantize_append(const kvq_cache_desc* cache, const void* k, const void* v,
+                               kvq_dtype in_dtype, int64_t n_tokens, const int64_t* slot_mapping,
+                               const void* t_k, kvq_dtype t_dtype, void* stream) {
+  g_last_error.clear();
+  if (n_tokens < 0) return fail(KVQ_ERR_INVALID_ARG, "n_tokens must be >= 0");
+  kvq_status s = check_cache(cache, n_tokens > 0, n_tokens > 0);
+  if (s != KVQ_OK) return s;
+  if ((s = check_quantizer(cache->quant_k, cache->alpha_k, cache->p_lo, cache->p_hi)) != KVQ_OK) return s;
+  if ((s = check_quantizer(cache->quant_v, cache->alpha_v, cache->p_lo, cache->p_hi)) != KVQ_OK) return s;
+  if (!valid_dtype(in_dtype)) return fail(KVQ_ERR_INVALID_ARG, "unknown input dtype");
+  if (t_k && t_dtype != in_dtype) return fail(KVQ_ERR_UNSUPPORTED, "t_dtype must equal in_dtype");
+  if (n_tokens == 0) return KVQ_OK;
+  if (!k || !v || !slot_mapping) return fail(KVQ_ERR_INVALID_ARG, "k, v and slot_mapping must be non-null");
+  if ((n_tokens + 127) / 128 > 0x7FFFFFFFLL) return fail(KVQ_ERR_UNSUPPORTED, "too many tokens");
+  kvq::AppendParams p{};
+  p.k = k; p.v = v; p.slots = slot_mapping; p.t = t_k;
+  p.kpool = static_cast<uint8_t*>(cache->k_pages);
+  p.vpool = static_cast<uint8_t*>(cache->v_pages);
+  p.n = n_tokens; p.num_pages = cache->num_pages; p.heads = cache->num_kv_heads;
+  p.bits_k = cache->bits_k; p.bits_v = cache->bits_v;
+  p.quant_k = cache->quant_k; p.quant_v = cache->quant_v;
+  percentile_position(cache->p_lo, &p.ilo, &p.flo);
+  percentile_position(cache->p_hi, &p.ihi, &p.fhi);
+  p.alpha_k = cache->alpha_k; p.alpha_v = cache->alpha_v;
+  return hip_status(kvq::launch_append(p, (int)in_dtype, static_cast<hipStream_t>(stream)));
+}
+
+size_t kvq_decode_workspace_bytes(const kvq_cache_desc* cache, int32_t batch, int32_t num_q_heads,
+                                  int32_t max_seq_len) {
+  if (!cache || cache->num_kv_heads < 1 || batch <= 0 || num_q_heads < 1 || max_seq_len < 0) return 0;
+  const kvq::DecodeSplit sp = kvq::decode_split(batch, cache->num_kv_heads, max_seq_len);
+  return workspace_layout(batch, num_q_heads, sp.chunks).total;
+}
+
+kvq_status kvq_decode_attn(const kvq_cache_desc* cache, const void* q, kvq_dtype q_dtype, int32_t batch,
+                           int32_t num_q_heads, const float* t_k_inv_t, const int32_t* block_table,
+                           int32_t max_pages, const int32_t* seq_lens, int32_t max_seq_len, float sm_scale,
+                           float* out, void* workspace, size_t workspace_bytes, void* stream) {
+  g_last_error.clear();
+  if (batch < 0) return fail(KVQ_ERR_INVALID_ARG, "batch must be >= 0");
+  kvq_status s = check_cache(cache, batch > 0, batch > 0);
+  if (s != KVQ_OK) return s;
+  if (num_q_heads < 1 || num_q_heads % cache->num_kv_heads != 0)
+    return fail(KVQ_ERR_INVALID_ARG, "num_q_heads must be a positive multiple of num_kv_heads");
+  const int group = num_q_heads / cache->num_kv_heads;
+  if (group > 16) return fail(KVQ_ERR_UNSUPPORTED, "at most 16 query heads per KV head");
+  if (!valid_dtype(q_dtype)) return fail(KVQ_ERR_INVALID_ARG, "unknown query dtype");
+  if (max_seq_len < 0 || max_pages < 0) return fail(KVQ_ERR_INVALID_ARG, "max_seq_len and max_pages must be >= 0");
+  if ((int64_t)max_pages * 64 < (int64_t)max_seq_len)
+    return fail(KVQ_ERR_INVALID_ARG, "max_pages*64 must cover max_seq_len");
+  if (!std::isfinite(sm_scale)) return fail(KVQ_ERR_INVALID_ARG, "sm_scale must be finite");
+  if (batch == 0) return KVQ_OK;
+  if (batch > 65535) return fail(KVQ_ERR_UNSUPPORTED, "batch must be <= 65535");
+  if (!q || !block_table || !seq_lens || !out)
+    return fail(KVQ_ERR_INVALID_ARG, "q, block_table, seq_lens and out must be non-null");
+  const kvq::DecodeSplit sp = kvq::decode_split(batch, cache->num_kv_heads, max_seq_len);
+  const WorkspaceLayout wl = workspace_layout(batch, num_q_heads, sp.chunks);
+  if (wl.total > 0 && (!workspace || workspace_bytes < wl.total))
+    return fail(KVQ_ERR_WORKSPACE, "workspace smaller than kvq_decode_workspace_bytes()");
+  kvq::DecodeParams p{};
+  p.kpool = static_cast<const uint8_t*>(cache->k_pages);
+  p.vpool = static_cast<const uint8_t*>(cache->v_pages);
+  p.q = q; p.tinv = t_k_inv_t; p.block_table = block_table; p.seq_lens = seq_lens; p.out = out;
+  p.ws_o = wl.total ? static_cast<float*>(workspace) : nullptr;
+  p.ws_ml = wl.total ? reinterpret_cast<float*>(static_cast<char*>(workspace) + wl.o_bytes) : nullptr;
+  p.batch = batch; p.heads_q = num_q_heads; p.heads_kv = cache->num_kv_heads; p.group = group;
+  p.max_pages = max_pages; p.num_pages = cache->num_pages; p.pages_per_wave = sp.pages_per_wave; p.chunks = sp.chunks;
+  p.score_scale = sm_scale * 1.4426950408889634f;
+  return hip_status(kvq::launch_decode(p, cache->bits_k, cache->bits_v, (int)q_dtype,
+                                       static_cast<hipStream_t>(stream)));
+}
+
+kvq_status kvq_dequant(const kvq_cache_desc* cache, int32_t which, const int64_t* slots, int64_t n_tokens,
+                       float* out, void* stream) {
+  g_last_error.clear();
+  if (which != 0 && which != 1) return fail(KVQ_ERR_INVALID_ARG, "which must be 0 (keys) or 1 (values)");
+  if (n_tokens < 0) return fail(KVQ_ERR_INVALID_ARG, "n_tokens must be >= 0");
+  kvq_status s = check_cache(cache, n_tokens > 0 && which == 0, n_tokens > 0 && which == 1);
+  if (s != KVQ_OK) return s;
+  if (n_tokens == 0) return KVQ_OK;
+  if (!slots || !out) return fail(KVQ_ERR_INVALID_ARG, "slots and out must be non-null");
+  if ((n_tokens * cache->num_kv_heads * 32 + 255) / 256 > 0x7FFFFFFFLL)
+    return fail(KVQ_ERR_UNSUPPORTED, "too many tokens");
+  kvq::DequantParams p{};
+  p.pool = static_cast<const uint8_t*>(which == 0 ? cache->k_pages : cache->v_pages);
+  p.slots = slots; p.out = out; p.n = n_tokens; p.num_pages = cache->num_pages;
+  p.heads = cache->num_kv_heads;
+  p.bits = which == 0 ? cache->bits_k : cache->bits_v;
+  p.which = which;
+  return hip_status(kvq::launch_dequant(p, static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

@@ -1,0 +1,459 @@
+// Write path: key transform after RoPE, per-token group clip, fp16 scale/zero,
+// codes, and packing into the fixed-width paged cache.
+//
+// Method: "WUSH-KV: KV Cache Quantization with Data-Adaptive Transforms" §4.2 (dense
+// per-KV-head key transform applied online after RoPE; values arrive already in the
+// folded basis), §4.3 (QuEST: the group is one token's 128 channels, RMS-based clip),
+// §5.3 (OSCAR-style percentile-clipped affine codes).  Layout: "Spend Bits Where
+// Queries Look" (NOVA-KV project page), "Three requirements": every token takes the
+// same number of bits in a paged cache.
+//
+// Work decomposition (gfx950, wave64).  A workgroup of 4 waves handles 128 consecutive
+// tokens of one KV head; each wave handles 32 tokens.  Lane l owns token l%32 and the
+// channel half hh = l/32 (channels 64*hh .. 64*hh+63), so a token's group lives in
+// two lanes and everything except one cross-lane exchange per group stays in-lane:
+//   * transform: D[out-channel][token] = T^T[out][in] . K^T[in][token] on the matrix
+//     cores (32x32x16, bf16 or f16, fp32 accumulate); the rows of T^T are permuted so
+//     that accumulator register r of M-tile mt on lane half hh is channel
+//     64*hh + 16*mt + r.  T^T is staged once per workgroup in LDS.
+//   * percentile clip: bottom-K / top-K insertion networks (v_med3) over the lane's
+//     64 values, one exchange with the partner lane, then the order statistics;
+//     order statistics do not depend on how they are found.  Positions outside the
+//     K smallest/largest use a 128-element bitonic sort across the wavefront.
+//   * rms clip: in-lane pairwise tree over the half, one exchange, correctly rounded
+//     sqrt.
+//   * keys: each lane writes its half of the token's row (16 or 32 bytes).
+//   * values: when the wave's 32 tokens fill an aligned run of one page, codes are
+//     transposed through LDS and whole words are stored; otherwise each code is
+//     merged into its word with atomic AND/OR so other tokens' bits survive.
+#include "kvq_device.h"
+#include "kvq_internal.h"
+
+namespace kvq {
+namespace {
+
+constexpr int kTileTokens = 32;
+constexpr int kWavesPerBlock = 4;
+constexpr int kBlockTokens = kTileTokens * kWavesPerBlock;
+constexpr int kTtStride = 136;   // padded LDS row of T^T (elements): spreads banks
+
+template <typename T> struct Mfma;
+template <> struct Mfma<__bf16> {
+  typedef bf16x8 vec;
+  static __device__ __forceinline__ f32x16 mma(vec a, vec b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+  }
+};
+template <> struct Mfma<_Float16> {
+  typedef half8 vec;
+  static __device__ __forceinline__ f32x16 mma(vec a, vec b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+  }
+};
+
+__device__ __forceinline__ void wave_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+}
+
+__device__ __forceinline__ float half_lo_to_f32(uint32_t w, bool bf16) {
+  return bf16 ? __uint_as_float(w << 16) : f16_bits_to_f32(w & 0xFFFFu);
+}
+__device__ __forceinline__ float half_hi_to_f32(uint32_t w, bool bf16) {
+  return bf16 ? __uint_as_float(w & 0xFFFF0000u) : f16_bits_to_f32(w >> 16);
+}
+
+// 64 consecutive elements (the lane's half of a token's row) as fp32.
+template <typename TIn>
+__device__ __forceinline__ void load_half_row(const TIn* src, float (&x)[64]) {
+  if constexpr (sizeof(TIn) == 4) {
+    const f32x4* p = reinterpret_cast<const f32x4*>(src);
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      f32x4 w = p[q];
+      x[4 * q] = w[0]; x[4 * q + 1] = w[1]; x[4 * q + 2] = w[2]; x[4 * q + 3] = w[3];
+    }
+  } else {
+    constexpr bool bf = __is_same(TIn, __bf16);
+    const u32x4* p = reinterpret_cast<const u32x4*>(src);
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      u32x4 w = p[q];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        x[8 * q + 2 * e] = half_lo_to_f32(w[e], bf);
+        x[8 * q + 2 * e + 1] = half_hi_to_f32(w[e], bf);
+      }
+    }
+  }
+}
+
+// k' = k . T on the matrix cores for the wave's 32 tokens.  tok_row: this lane's token
+// row (128 elements of the head).  tt: T^T of the head in LDS.
+template <typename TIn>
+__device__ __forceinline__ void transform_mfma(const TIn* tok_row, const uint16_t* tt, int lane,
+                                               float (&x)[64]) {
+  typedef typename Mfma<TIn>::vec vec;
+  const int rho = lane & 31, kk = lane >> 5;
+  f32x16 acc[4];
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt) acc[mt] = f32x16{};
+#pragma unroll
+  for (int ks = 0; ks < 8; ++ks) {
+    u32x4 braw = *reinterpret_cast<const u32x4*>(tok_row + 16 * ks + 8 * kk);
+    vec b = __builtin_bit_cast(vec, braw);
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) {
+      const int ch = 64 * ((rho >> 2) & 1) + 16 * mt + 4 * (rho >> 3) + (rho & 3);
+      u32x4 araw = *reinterpret_cast<const u32x4*>(tt + ch * kTtStride + 16 * ks + 8 * kk);
+      acc[mt] = Mfma<TIn>::mma(__builtin_bit_cast(vec, araw), b, acc[mt]);
+    }
+  }
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) x[16 * mt + r] = acc[mt][r];
+}
+
+// fp32 inputs: k' = k . T with fp32 fused multiply-adds (c ascending).
+__device__ __forceinline__ void transform_f32(const float* tok_row, const float* t_head, int hh,
+                                              float (&x)[64]) {
+#pragma unroll
+  for (int m = 0; m < 64; ++m) x[m] = 0.0f;
+  for (int c = 0; c < kHeadDim; ++c) {
+    const float kc = tok_row[c];
+    const f32x4* tr = reinterpret_cast<const f32x4*>(t_head + c * kHeadDim + 64 * hh);
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      f32x4 w = tr[q];
+      x[4 * q] = __builtin_fmaf(kc, w[0], x[4 * q]);
+      x[4 * q + 1] = __builtin_fmaf(kc, w[1], x[4 * q + 1]);
+      x[4 * q + 2] = __builtin_fmaf(kc, w[2], x[4 * q + 2]);
+      x[4 * q + 3] = __builtin_fmaf(kc, w[3], x[4 * q + 3]);
+    }
+  }
+}
+
+// Smallest / largest K values of the token's 128 (lane + partner lane), sorted:
+// lo[k] = s[k], hi[k] = s[127-k].
+template <int K>
+__device__ __forceinline__ void select_extremes(const float (&x)[64], float (&lo)[K], float (&hi)[K]) {
+#pragma unroll
+  for (int k = 0; k < K; ++k) { lo[k] = __builtin_inff(); hi[k] = -__builtin_inff(); }
+#pragma unroll
+  for (int m = 0; m < 64; ++m) {
+    const float v = x[m];
+#pragma unroll
+    for (int k = K - 1; k >= 1; --k) {
+      lo[k] = __builtin_amdgcn_fmed3f(lo[k - 1], lo[k], v);
+      hi[k] = __builtin_amdgcn_fmed3f(hi[k - 1], hi[k], v);
+    }
+    lo[0] = fminf(lo[0], v);
+    hi[0] = fmaxf(hi[0], v);
+  }
+  float plo[K], phi[K];
+#pragma unroll
+  for (int k = 0; k < K; ++k) { plo[k] = __shfl_xor(lo[k], 32); phi[k] = __shfl_xor(hi[k], 32); }
+#pragma unroll
+  for (int j = 0; j < K; ++j) {
+#pragma unroll
+    for (int k = K - 1; k >= 1; --k) {
+      lo[k] = __builtin_amdgcn_fmed3f(lo[k - 1], lo[k], plo[j]);
+      hi[k] = __builtin_amdgcn_fmed3f(hi[k - 1], hi[k], phi[j]);
+    }
+    lo[0] = fminf(lo[0], plo[j]);
+    hi[0] = fmaxf(hi[0], phi[j]);
+  }
+}
+
+template <int K>
+__device__ __forceinline__ float order_stat(const float (&lo)[K], const float (&hi)[K], int r) {
+  float v = lo[0];
+#pragma unroll
+  for (int k = 0; k < K; ++k) {
+    v = (r == k) ? lo[k] : v;
+    v = (r == kHeadDim - 1 - k) ? hi[k] : v;
+  }
+  return v;
+}
+
+#pragma clang fp contract(off)
+
+__device__ __forceinline__ float interpolate(float s0, float s1, float f) {
+  return __builtin_fmaf(f, s1 - s0, s0) + 0.0f;
+}
+
+// Sum of squares of the token's 128 values: each lane's half by a pairwise tree
+// (stride 32..1), then the two halves added.
+__device__ __forceinline__ float rms_bound(const float (&x)[64], float alpha) {
+  float sq[64];
+#pragma unroll
+  for (int m = 0; m < 64; ++m) sq[m] = x[m] * x[m];
+#pragma unroll
+  for (int stride = 32; stride >= 1; stride >>= 1)
+#pragma unroll
+    for (int m = 0; m < stride; ++m) sq[m] = sq[m] + sq[m + stride];
+  const float total = sq[0] + __shfl_xor(sq[0], 32);
+  const float rms = sqrtf(total / 128.0f);
+  return alpha * rms;
+}
+
+__device__ __forceinline__ float sat_f16(float v) { return fminf(fmaxf(v, -65504.0f), 65504.0f); }
+
+struct GroupQuant {
+  float zf, r, lmax;
+  uint16_t s16, z16;
+};
+
+__device__ __forceinline__ GroupQuant make_quant(float lo, float hi, int bits) {
+  GroupQuant g;
+  g.lmax = (float)((1 << bits) - 1);
+  const float s = (hi - lo) / g.lmax;
+  g.s16 = f32_to_f16_bits(sat_f16(s));
+  g.z16 = f32_to_f16_bits(sat_f16(lo));
+  const float sf = f16_bits_to_f32(g.s16);
+  g.zf = f16_bits_to_f32(g.z16);
+  g.r = (sf == 0.0f) ? 0.0f : 1.0f / sf;
+  return g;
+}
+
+__device__ __forceinline__ uint32_t code_of(float x, const GroupQuant& g) {
+  const float t = (x - g.zf) * g.r;
+  return (uint32_t)__builtin_amdgcn_fmed3f(rintf(t), 0.0f, g.lmax);
+}
+
+#pragma clang fp contract(on)
+
+// Clip bounds of the lane's token (both lanes of the token get the same values).
+// The bitonic path sorts each token of the wave in turn through a 128-float LDS buffer.
+template <int KSEL>
+__device__ __forceinline__ void clip_bounds(const float (&x)[64], int quant, float alpha, int ilo,
+                                            int ihi, float flo, float fhi, int lane, float* sortbuf,
+                                            float& lo, float& hi) {
+  if (quant == 1) {
+    const float cl = rms_bound(x, alpha);
+    lo = -cl;
+    hi = cl;
+    return;
+  }
+  const int ilo1 = ilo + 1 < kHeadDim ? ilo + 1 : kHeadDim - 1;
+  const int ihi1 = ihi + 1 < kHeadDim ? ihi + 1 : kHeadDim - 1;
+  if constexpr (KSEL > 0) {
+    float bl[KSEL], bh[KSEL];
+    select_extremes<KSEL>(x, bl, bh);
+    lo = interpolate(order_stat<KSEL>(bl, bh, ilo), order_stat<KSEL>(bl, bh, ilo1), flo);
+    hi = interpolate(order_stat<KSEL>(bl, bh, ihi), order_stat<KSEL>(bl, bh, ihi1), fhi);
+  } else {
+    const int hh = lane >> 5;
+    lo = 0.0f;
+    hi = 0.0f;
+    for (int tok = 0; tok < kTileTokens; ++tok) {
+      if ((lane & 31) == tok) {
+#pragma unroll
+        for (int m = 0; m < 64; ++m) sortbuf[64 * hh + m] = x[m];
+      }
+      wave_sync();
+      float a = sortbuf[lane], b = sortbuf[lane + 64];
+      // bitonic network over element indices i = lane (a) and i = lane + 64 (b)
+      for (int k = 2; k <= kHeadDim; k <<= 1) {
+        for (int j = k >> 1; j >= 1; j >>= 1) {
+          if (j == 64) {
+            const float mn = fminf(a, b), mx = fmaxf(a, b);
+            a = mn;
+            b = mx;
+          } else {
+            const float pa = __shfl_xor(a, j), pb = __shfl_xor(b, j);
+            const bool up_a = (lane & k) == 0, up_b = ((lane + 64) & k) == 0;
+            const bool low = (lane & j) == 0;
+            a = (low == up_a) ? fminf(a, pa) : fmaxf(a, pa);
+            b = (low == up_b) ? fminf(b, pb) : fmaxf(b, pb);
+          }
+        }
+      }
+      wave_sync();
+      sortbuf[lane] = a;
+      sortbuf[lane + 64] = b;
+      wave_sync();
+      if ((lane & 31) == tok) {
+        lo = interpolate(sortbuf[ilo], sortbuf[ilo1], flo);
+        hi = interpolate(sortbuf[ihi], sortbuf[ihi1], fhi);
+      }
+      wave_sync();
+    }
+  }
+}
+
+template <typename TIn, int KSEL>
+__global__ __launch_bounds__(256) void append_kernel(AppendParams p) {
+  __shared__ __attribute__((aligned(16))) uint16_t tt[kHeadDim * kTtStride];
+  __shared__ __attribute__((aligned(16))) uint32_t vbuf[kWavesPerBlock][kTileTokens * 32];
+  __shared__ float sortbuf[kWavesPerBlock][kHeadDim];
+
+  const int h = blockIdx.y;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int tl = lane & 31, hh = lane >> 5;
+  const int64_t tile0 = (int64_t)blockIdx.x * kBlockTokens + wave * kTileTokens;
+  const int64_t i = tile0 + tl;
+  const bool in_range = i < p.n;
+  const int64_t i_ld = in_range ? i : p.n - 1;
+  const int64_t slot = in_range ? p.slots[i] : -1;
+  const bool valid = slot >= 0 && slot < p.num_pages * kPageTokens;   // others are skipped
+  const int64_t page = valid ? slot / kPageTokens : 0;
+  const int o = valid ? (int)(slot % kPageTokens) : 0;
+
+  const TIn* krow = reinterpret_cast<const TIn*>(p.k) + (i_ld * p.heads + h) * kHeadDim;
+  const TIn* vrow = reinterpret_cast<const TIn*>(p.v) + (i_ld * p.heads + h) * kHeadDim;
+  constexpr bool kMfmaType = sizeof(TIn) == 2;
+
+  if constexpr (kMfmaType) {
+    if (p.t != nullptr) {
+      const TIn* th = reinterpret_cast<const TIn*>(p.t) + (int64_t)h * kHeadDim * kHeadDim;
+      for (int idx = threadIdx.x; idx < kHeadDim * 16; idx += 256) {
+        const int c = idx >> 4, j0 = (idx & 15) * 8;
+        u32x4 w = *reinterpret_cast<const u32x4*>(th + c * kHeadDim + j0);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          tt[(j0 + 2 * e) * kTtStride + c] = (uint16_t)(w[e] & 0xFFFFu);
+          tt[(j0 + 2 * e + 1) * kTtStride + c] = (uint16_t)(w[e] >> 16);
+        }
+      }
+      __syncthreads();
+    }
+  }
+
+  float x[64];
+  float lo, hi;
+
+  // ---------------- keys ----------------
+  if (p.t == nullptr) {
+    load_half_row<TIn>(krow + 64 * hh, x);
+  } else if constexpr (kMfmaType) {
+    transform_mfma<TIn>(krow, tt, lane, x);
+  } else {
+    transform_f32(reinterpret_cast<const float*>(krow),
+                  reinterpret_cast<const float*>(p.t) + (int64_t)h * kHeadDim * kHeadDim, hh, x);
+  }
+  clip_bounds<KSEL>(x, p.quant_k, p.alpha_k, p.ilo, p.ihi, p.flo, p.fhi, lane, sortbuf[wave], lo, hi);
+  {
+    const GroupQuant g = make_quant(lo, hi, p.bits_k);
+    uint8_t* blk = p.kpool + (page * p.heads + h) * (int64_t)block_bytes(p.bits_k);
+    if (valid) {
+      if (p.bits_k == 2) {
+        u32x4 w;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          uint32_t acc = 0;
+#pragma unroll
+          for (int e = 0; e < 16; ++e) acc |= code_of(x[16 * q + e], g) << (2 * e);
+          w[q] = acc;
+        }
+        *reinterpret_cast<u32x4*>(blk + o * 32 + 16 * hh) = w;
+      } else {
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+          u32x4 w;
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            uint32_t acc = 0;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) acc |= code_of(x[32 * half + 8 * q + e], g) << (4 * e);
+            w[q] = acc;
+          }
+          *reinterpret_cast<u32x4*>(blk + o * 64 + 32 * hh + 16 * half) = w;
+        }
+      }
+      uint16_t* meta = reinterpret_cast<uint16_t*>(blk + code_bytes(p.bits_k));
+      meta[hh * kPageTokens + o] = hh ? g.z16 : g.s16;
+    }
+  }
+
+  // ---------------- values ----------------
+  load_half_row<TIn>(vrow + 64 * hh, x);
+  clip_bounds<KSEL>(x, p.quant_v, p.alpha_v, p.ilo, p.ihi, p.flo, p.fhi, lane, sortbuf[wave], lo, hi);
+  const GroupQuant g = make_quant(lo, hi, p.bits_v);
+  const int bits = p.bits_v;
+  const int64_t vbb = block_bytes(bits);
+  uint8_t* blk = p.vpool + (page * p.heads + h) * vbb;
+  if (valid) {
+    uint16_t* meta = reinterpret_cast<uint16_t*>(blk + code_bytes(bits));
+    meta[hh * kPageTokens + o] = hh ? g.z16 : g.s16;
+  }
+  const int64_t slot0 = __shfl(slot, 0);
+  const bool aligned_run = __all(valid && slot == slot0 + tl) && (slot0 % kTileTokens) == 0;
+  if (aligned_run) {
+    // codes as bytes [token][channel] in LDS, then whole words of 32/bits tokens
+    uint32_t* vb = vbuf[wave];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      u32x4 w;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int m = 16 * q + 4 * e;
+        w[e] = code_of(x[m], g) | (code_of(x[m + 1], g) << 8) | (code_of(x[m + 2], g) << 16) |
+               (code_of(x[m + 3], g) << 24);
+      }
+      *reinterpret_cast<u32x4*>(vb + tl * 32 + 16 * hh + 4 * q) = w;
+    }
+    wave_sync();
+    const int o0 = (int)(slot0 % kPageTokens);
+    const int cq = lane & 31, part = lane >> 5;
+    uint32_t* words = reinterpret_cast<uint32_t*>(p.vpool + ((slot0 / kPageTokens) * p.heads + h) * vbb);
+    const int per_word = 32 / bits;
+    const int rows = kTileTokens / per_word;        // word rows written by the wave
+    for (int rw = part; rw < rows; rw += 2) {
+      u32x4 w = {0u, 0u, 0u, 0u};
+      for (int t = 0; t < per_word; ++t) {
+        const uint32_t d = vb[(rw * per_word + t) * 32 + cq];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) w[e] |= ((d >> (8 * e)) & 0xFFu) << (bits * t);
+      }
+      *reinterpret_cast<u32x4*>(words + (o0 / per_word + rw) * kHeadDim + 4 * cq) = w;
+    }
+  } else if (valid) {
+    uint32_t* words = reinterpret_cast<uint32_t*>(blk);
+    const int per_word = 32 / bits;
+    const int row = o / per_word, sh = (o % per_word) * bits;
+    const uint32_t mask = ((1u << bits) - 1u) << sh;
+#pragma unroll
+    for (int m = 0; m < 64; ++m) {
+      uint32_t* w = words + row * kHeadDim + 64 * hh + m;
+      atomicAnd(w, ~mask);
+      atomicOr(w, code_of(x[m], g) << sh);
+    }
+  }
+}
+
+template <typename TIn>
+hipError_t launch_typed(const AppendParams& p, hipStream_t stream) {
+  dim3 grid((unsigned)((p.n + kBlockTokens - 1) / kBlockTokens), (unsigned)p.heads);
+  dim3 block(256);
+  // order statistics needed from the sorted group: ilo, ilo+1, ihi, ihi+1
+  auto reach = [](int r) { return r < kHeadDim / 2 ? r + 1 : kHeadDim - r; };
+  int need = 0;
+  if (p.quant_k == 0 || p.quant_v == 0) {
+    const int rs[4] = {p.ilo, p.ilo + 1 < kHeadDim ? p.ilo + 1 : kHeadDim - 1, p.ihi,
+                       p.ihi + 1 < kHeadDim ? p.ihi + 1 : kHeadDim - 1};
+    for (int r : rs) need = reach(r) > need ? reach(r) : need;
+  }
+  if (need <= 3) {
+    hipLaunchKernelGGL((append_kernel<TIn, 3>), grid, block, 0, stream, p);
+  } else if (need <= 8) {
+    hipLaunchKernelGGL((append_kernel<TIn, 8>), grid, block, 0, stream, p);
+  } else {
+    hipLaunchKernelGGL((append_kernel<TIn, 0>), grid, block, 0, stream, p);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_append(const AppendParams& p, int in_dtype, hipStream_t stream) {
+  switch (in_dtype) {
+    case 0: return launch_typed<float>(p, stream);
+    case 1: return launch_typed<__bf16>(p, stream);
+    default: return launch_typed<_Float16>(p, stream);
+  }
+}
+
+}  // namespace kvq

@@ -1,0 +1,68 @@
+// Host-side declarations shared by the C-ABI layer and the kernel launchers.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kvq {
+
+struct AppendParams {
+  const void* k;
+  const void* v;
+  const int64_t* slots;
+  const void* t;          // [H][128][128] or null
+  uint8_t* kpool;
+  uint8_t* vpool;
+  int64_t n;
+  int64_t num_pages;
+  int heads;
+  int bits_k, bits_v;
+  int quant_k, quant_v;   // 0 percentile, 1 rms
+  int ilo, ihi;           // percentile order-statistic positions (0..127)
+  float flo, fhi;         // interpolation weights
+  float alpha_k, alpha_v;
+};
+
+struct DecodeParams {
+  const uint8_t* kpool;
+  const uint8_t* vpool;
+  const void* q;
+  const float* tinv;      // [Hkv][128][128] or null
+  const int32_t* block_table;
+  const int32_t* seq_lens;
+  float* out;             // [B][Hq][128]
+  float* ws_o;            // [B][Hq][chunks][128]
+  float* ws_ml;           // [B][Hq][chunks][2]
+  int batch, heads_q, heads_kv, group;
+  int max_pages;          // row stride of block_table
+  int64_t num_pages;      // pages in each pool (page ids outside are skipped)
+  int pages_per_wave;
+  int chunks;             // workgroups per (sequence, KV head)
+  float score_scale;      // sm_scale * log2(e)
+};
+
+struct DequantParams {
+  const uint8_t* pool;
+  const int64_t* slots;
+  float* out;
+  int64_t n;
+  int64_t num_pages;
+  int heads;
+  int bits;
+  int which;
+};
+
+// Kernel launchers; return hipSuccess or the launch error.
+hipError_t launch_append(const AppendParams& p, int in_dtype, hipStream_t stream);
+hipError_t launch_decode(const DecodeParams& p, int bits_k, int bits_v, int q_dtype,
+                         hipStream_t stream);
+hipError_t launch_dequant(const DequantParams& p, hipStream_t stream);
+
+// Split of a decode launch, a function of the shapes only.
+struct DecodeSplit {
+  int pages_per_wave;
+  int chunks;
+};
+DecodeSplit decode_split(int batch, int heads_kv, int max_seq_len);
+
+}  // namespace kvq

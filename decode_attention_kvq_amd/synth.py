@@ -95,8 +95,13 @@ def bf16_round(x: np.ndarray) -> np.ndarray:
 
 
 def to_dtype(x: np.ndarray, dtype: str) -> np.ndarray:
+    """Round fp32 values to the workload's input type ("f32", "bf16" or "f16"), as fp32."""
     x = np.asarray(x, np.float32)
-    return bf16_round(x) if dtype == "bf16" else x
+    if dtype == "bf16":
+        return bf16_round(x)
+    if dtype == "f16":
+        return x.astype(np.float16).astype(np.float32)
+    return x
 
 
 def haar_orthogonal(d: int, rng: np.random.Generator) -> np.ndarray:

@@ -1,0 +1,157 @@
+/*
+ * kvq.h -- C ABI of the quantized KV-cache library for AMD Instinct MI355X (gfx950).
+ *
+ * Two operations, as the method's pages state the problem:
+ *   write path  -- "WUSH-KV: KV Cache Quantization with Data-Adaptive Transforms",
+ *                  §4.2 (dense per-KV-head key transform applied after RoPE; the value
+ *                  transform is folded into W_V/W_O offline, so values arrive already
+ *                  transformed), §4.3 (QuEST: one group = one token's d channels,
+ *                  RMS-based clip) and §5.3 (OSCAR-style percentile-clipped affine
+ *                  codes); "Spend Bits Where Queries Look" (NOVA-KV project page),
+ *                  "Three requirements" (paged cache, same number of bits per token)
+ *                  and its online-inference figure (encode once when written).
+ *   read path   -- same pages: query-side compensation q' = q T^-T (§4.2), decode
+ *                  inside attention on every step (NOVA-KV "Three requirements": read
+ *                  cost is paid over the whole cache each step), grouped-query
+ *                  attention (§4.1); the output stays in the transformed value basis
+ *                  that W_O absorbs (§4.2).
+ *
+ * Conventions for every entry point
+ *   - Pointers marked "device" are HIP device memory owned by the caller; the library
+ *     never allocates, frees or keeps them.  "stream" is a hipStream_t (NULL = the
+ *     default stream).  Work is enqueued asynchronously; the call returns when it is
+ *     enqueued.  Device-side faults surface at the caller's next synchronisation.
+ *   - Arguments are validated on the host before anything is enqueued; a non-OK status
+ *     means nothing was enqueued.  kvq_last_error() then returns a message for the
+ *     calling thread.
+ *   - Shapes are fixed by the layout: head_dim 128, page_size 64 tokens, 2- or 4-bit
+ *     codes.  Other values return KVQ_ERR_UNSUPPORTED.
+ *   - Floating-point inputs must be finite.
+ *
+ * Page layout (the ABI of k_pages / v_pages).  A pool is [num_pages][num_kv_heads]
+ * blocks of kvq_block_bytes(bits) bytes; the block of (page p, KV head h) starts at
+ * pool + (p*num_kv_heads + h)*kvq_block_bytes(bits).  Token slot s lives in page
+ * s/64 at offset o = s%64.  A block holds, in order:
+ *   codes   64*128*bits/8 bytes of little-endian 32-bit words, R = 32/bits codes a word
+ *           keys:   word o*(128/R) + c/R,  bits (c%R)*bits   (token-major rows)
+ *           values: word (o/R)*128 + c,    bits (o%R)*bits   (a word holds R
+ *                   consecutive tokens of one channel c)
+ *   scales  64 fp16 (token o at byte 2*o of this section)
+ *   zeros   64 fp16 (token o at byte 2*o of this section)
+ * A dequantized element is fma(code, scale, zero) in fp32.  2-bit blocks are 2304 bytes
+ * (2.25 bits per element), 4-bit blocks 4352 bytes (4.25 bits per element).
+ *
+ * Quantizer of one group x[0..127] (one token of one KV head):
+ *   percentile: lo, hi = linear-interpolated order statistics at p_lo, p_hi
+ *               (rank p*127 formed in double, weight f rounded to float,
+ *               v = fmaf(f, s[i+1] - s[i], s[i]) + 0.0f over the sorted values s)
+ *   rms:        lo = -alpha*r, hi = +alpha*r, r = sqrtf(sum(x^2)/128) with the sum
+ *               taken as two 64-element halves, each summed by a pairwise tree
+ *               (stride 32, 16, ..., 1), then added
+ *   then        s = (hi - lo)/L (L = 2^bits - 1), scale = fp16(s), zero = fp16(lo)
+ *               (both saturated to +-65504, round to nearest even),
+ *               r = scale == 0 ? 0 : 1/scale, code = clamp(rint((x - zero)*r), 0, L).
+ */
+#ifndef KVQ_H
+#define KVQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum kvq_status {
+  KVQ_OK = 0,
+  KVQ_ERR_INVALID_ARG = -1,   /* null pointer, negative size, inconsistent shapes */
+  KVQ_ERR_UNSUPPORTED = -2,   /* valid but not implemented: head_dim, bits, dtype pair */
+  KVQ_ERR_WORKSPACE = -3,     /* workspace missing or smaller than required */
+  KVQ_ERR_HIP = -4            /* a HIP call failed while enqueueing */
+} kvq_status;
+
+typedef enum kvq_dtype { KVQ_F32 = 0, KVQ_BF16 = 1, KVQ_F16 = 2 } kvq_dtype;
+
+typedef enum kvq_quantizer {
+  KVQ_Q_PERCENTILE = 0,  /* OSCAR-style percentile-clipped affine (WUSH-KV §5.3) */
+  KVQ_Q_RMS = 1          /* QuEST-style RMS-clipped symmetric levels (WUSH-KV §4.3) */
+} kvq_quantizer;
+
+/* Geometry and quantizer settings of one layer's paged cache. */
+typedef struct kvq_cache_desc {
+  int32_t num_kv_heads;   /* >= 1 */
+  int32_t head_dim;       /* must be 128 */
+  int32_t page_size;      /* must be 64 */
+  int32_t bits_k;         /* 2 or 4 */
+  int32_t bits_v;         /* 2 or 4 */
+  int32_t quant_k;        /* kvq_quantizer for keys */
+  int32_t quant_v;        /* kvq_quantizer for values */
+  float p_lo, p_hi;       /* percentile quantizer: 0 <= p_lo <= p_hi <= 1 */
+  float alpha_k, alpha_v; /* rms quantizer clip multipliers, > 0 */
+  int64_t num_pages;      /* pages in each pool */
+  void* k_pages;          /* device, [num_pages][num_kv_heads][kvq_block_bytes(bits_k)] */
+  void* v_pages;          /* device, [num_pages][num_kv_heads][kvq_block_bytes(bits_v)] */
+} kvq_cache_desc;
+
+/* Bytes of one (page, KV head) block for 2- or 4-bit codes; 0 for other widths. */
+size_t kvq_block_bytes(int32_t bits);
+
+/* Write path: transform, clip, quantize and pack n_tokens new tokens.
+ *   k, v          device, [n_tokens][num_kv_heads][128] of in_dtype; keys post-RoPE,
+ *                 values already in the folded (transformed) basis.
+ *   slot_mapping  device, [n_tokens] int64; slot of each token.  Slots must be
+ *                 distinct; a slot < 0 or >= num_pages*64 is skipped (nothing written).
+ *   t_k           device, [num_kv_heads][128][128] row-major, k' = k . T_K; or NULL for
+ *                 the identity.  t_dtype must equal in_dtype (bf16 and f16 inputs use
+ *                 matrix cores with fp32 accumulation; f32 uses fp32 arithmetic).
+ * Bits of a block not belonging to the written tokens are preserved, so tokens may be
+ * appended one at a time into partly filled pages. */
+kvq_status kvq_quantize_append(const kvq_cache_desc* cache, const void* k, const void* v,
+                               kvq_dtype in_dtype, int64_t n_tokens,
+                               const int64_t* slot_mapping, const void* t_k,
+                               kvq_dtype t_dtype, void* stream);
+
+/* Workspace bytes kvq_decode_attn needs for these sizes (0 when none is needed). */
+size_t kvq_decode_workspace_bytes(const kvq_cache_desc* cache, int32_t batch,
+                                  int32_t num_q_heads, int32_t max_seq_len);
+
+/* Read path: one decode step of grouped-query attention over the quantized cache.
+ *   q            device, [batch][num_q_heads][128] of q_dtype (post-RoPE queries);
+ *                num_q_heads must be a multiple of num_kv_heads, at most 16 query
+ *                heads per KV head; query head g reads KV head g/(num_q_heads/num_kv_heads).
+ *   t_k_inv_t    device, [num_kv_heads][128][128] fp32 row-major, q' = q . T_K^-T; NULL
+ *                when keys were written without a transform.
+ *   block_table  device, [batch][max_pages] int32 page ids; entries past a sequence's
+ *                last page are not read; a page id outside [0, num_pages) contributes
+ *                nothing (its tokens are skipped).
+ *   seq_lens     device, [batch] int32, 0 <= seq_lens[b] <= max_seq_len <= 64*max_pages
+ *                (max_seq_len sizes the split; a larger seq_lens[b] is clamped to
+ *                64*max_pages).
+ *   sm_scale     softmax scale (1/sqrt(128) for standard attention).
+ *   out          device, [batch][num_q_heads][128] fp32, in the transformed value basis;
+ *                an empty sequence gives zeros.
+ *   workspace    device scratch of at least kvq_decode_workspace_bytes(...) bytes. */
+kvq_status kvq_decode_attn(const kvq_cache_desc* cache, const void* q, kvq_dtype q_dtype,
+                           int32_t batch, int32_t num_q_heads, const float* t_k_inv_t,
+                           const int32_t* block_table, int32_t max_pages,
+                           const int32_t* seq_lens, int32_t max_seq_len, float sm_scale,
+                           float* out, void* workspace, size_t workspace_bytes,
+                           void* stream);
+
+/* Dequantize cached tokens: which = 0 keys (transformed basis), 1 values.
+ *   slots  device, [n_tokens] int64 (< 0 or >= num_pages*64: the output rows are left
+ *          untouched)
+ *   out    device, [n_tokens][num_kv_heads][128] fp32, fma(code, scale, zero). */
+kvq_status kvq_dequant(const kvq_cache_desc* cache, int32_t which, const int64_t* slots,
+                       int64_t n_tokens, float* out, void* stream);
+
+const char* kvq_status_string(kvq_status status);
+
+/* Message describing the calling thread's last non-OK status ("" if none). */
+const char* kvq_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KVQ_H */

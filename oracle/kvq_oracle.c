@@ -154,15 +154,18 @@ void oracle_clip_percentile(const float* x, int n, double p_lo, double p_hi, flo
 
 /* QuEST-style RMS clip ([W] §4.3): symmetric range [-alpha*rms, +alpha*rms] where
    rms = sqrt(mean(x^2)) over the group's n = 128 channels.  The fp32 sum of squares
-   is taken in a fixed pairwise order: at stride 64, 32, ..., 1 each element i < stride
-   adds element i + stride. */
+   is taken in a fixed order (the pages fix none): each half of the group (channels
+   0..63 and 64..127) is summed by a pairwise tree -- at stride 32, 16, ..., 1 element
+   i < stride of the half adds element i + stride -- and the two half sums are added. */
 void oracle_clip_rms(const float* x, int n, float alpha, float* lo, float* hi)
 {
     float sq[HEAD_DIM];
+    int half = n / 2;
     for (int i = 0; i < n; ++i) sq[i] = x[i] * x[i];
-    for (int stride = n / 2; stride >= 1; stride /= 2)
-        for (int i = 0; i < stride; ++i) sq[i] = sq[i] + sq[i + stride];
-    float rms = sqrtf(sq[0] / (float)n);
+    for (int h = 0; h < 2; ++h)
+        for (int stride = half / 2; stride >= 1; stride /= 2)
+            for (int i = 0; i < stride; ++i) sq[h * half + i] = sq[h * half + i] + sq[h * half + i + stride];
+    float rms = sqrtf((sq[0] + sq[half]) / (float)n);
     float cl = alpha * rms;
     *lo = -cl;
     *hi = cl;

@@ -1,0 +1,47 @@
+"""Shared helpers of the GPU parity tests (host side only)."""
+from __future__ import annotations
+
+import numpy as np
+
+import oracle
+
+
+def row_rel_err(got: np.ndarray, ref: np.ndarray) -> np.ndarray:
+    """Per (sequence, query head) row: max_j |got - ref| / max_j |ref|."""
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    num = np.max(np.abs(got - ref), axis=-1)
+    den = np.max(np.abs(ref), axis=-1)
+    return np.where(den > 0, num / np.where(den > 0, den, 1), num)
+
+
+def pool_codes(pool: np.ndarray, which: int, bits: int, slots):
+    """Codes, scale bits and zero bits of the given slots, read with the oracle's unpacker."""
+    H = pool.shape[1]
+    codes = np.zeros((len(slots), H, 128), np.uint8)
+    s = np.zeros((len(slots), H), np.uint16)
+    z = np.zeros((len(slots), H), np.uint16)
+    for i, slot in enumerate(slots):
+        p, o = divmod(int(slot), 64)
+        for h in range(H):
+            c, si, zi = oracle.unpack_token(pool[p, h], which, bits, o)
+            codes[i, h], s[i, h], z[i, h] = c, si, zi
+    return codes, s, z
+
+
+def f16_ulp_distance(a: np.ndarray, b: np.ndarray) -> np.ndarray:
+    """Distance in fp16 ulps between two arrays of fp16 bit patterns (same sign assumed
+    when both are non-zero)."""
+    def ordered(x):
+        x = x.astype(np.int64)
+        return np.where(x & 0x8000, -(x & 0x7FFF), x)
+    return np.abs(ordered(a) - ordered(b))
+
+
+def describe_mismatch(got: np.ndarray, ref: np.ndarray, limit: int = 8) -> str:
+    idx = np.argwhere(got != ref)
+    lines = [f"{len(idx)} of {got.size} differ"]
+    for k in idx[:limit]:
+        k = tuple(int(t) for t in k)
+        lines.append(f"  at {k}: got {got[k]!r} ref {ref[k]!r}")
+    return "\n".join(lines)

@@ -1,0 +1,129 @@
+"""Host-only checks of the C ABI: the library loads, exports every function the header
+declares, the descriptor layout matches the C compiler's, and invalid arguments are
+rejected before anything is enqueued (no GPU is touched)."""
+import ctypes as C
+import os
+import re
+import subprocess
+import tempfile
+
+import pytest
+
+from decode_attention_kvq_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kvq.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(_lib.LIB_PATH):
+        from decode_attention_kvq_amd import build
+        build.build()
+    return _lib.load()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(kvq_[a-z_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    assert set(names) == set(_lib.EXPORTS), names
+    for n in names:
+        assert hasattr(lib, n), n
+    out = subprocess.run(["nm", "-D", "--defined-only", _lib.LIB_PATH], capture_output=True, text=True).stdout
+    for n in names:
+        assert re.search(r"\bT %s$" % n, out, re.M), n
+
+
+def test_descriptor_layout_matches_c():
+    src = r"""
+    #include <stddef.h>
+    #include <stdio.h>
+    #include "kvq.h"
+    int main(void) {
+      printf("%zu %zu %zu %zu %zu\n", sizeof(kvq_cache_desc), offsetof(kvq_cache_desc, p_lo),
+             offsetof(kvq_cache_desc, num_pages), offsetof(kvq_cache_desc, k_pages),
+             offsetof(kvq_cache_desc, v_pages));
+      return 0;
+    }"""
+    with tempfile.TemporaryDirectory() as d:
+        c = os.path.join(d, "l.c")
+        exe = os.path.join(d, "l")
+        open(c, "w").write(src)
+        subprocess.check_call(["gcc", "-std=c11", "-I", os.path.join(ROOT, "include"), c, "-o", exe])
+        got = subprocess.check_output([exe]).decode().split()
+    D = _lib.KvqCacheDesc
+    assert [int(x) for x in got] == [C.sizeof(D), D.p_lo.offset, D.num_pages.offset,
+                                      D.k_pages.offset, D.v_pages.offset]
+
+
+def _desc(**kw):
+    d = dict(num_kv_heads=8, head_dim=128, page_size=64, bits_k=2, bits_v=2, quant_k=0, quant_v=0,
+             p_lo=0.01, p_hi=0.99, alpha_k=2.83, alpha_v=2.83, num_pages=4, k_pages=0x1000,
+             v_pages=0x2000)
+    d.update(kw)
+    return _lib.KvqCacheDesc(**d)
+
+
+def test_block_bytes_and_status_strings(lib):
+    assert lib.kvq_block_bytes(2) == 2304 and lib.kvq_block_bytes(4) == 4352
+    assert lib.kvq_block_bytes(3) == 0
+    assert lib.kvq_status_string(-3) == b"workspace too small"
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(head_dim=64), -2), (dict(page_size=32), -2), (dict(bits_k=3), -2), (dict(bits_v=8), -2),
+    (dict(num_kv_heads=0), -1), (dict(p_lo=0.5, p_hi=0.4), -1), (dict(p_hi=1.5), -1),
+    (dict(quant_k=1, alpha_k=0.0), -1), (dict(quant_v=7), -1), (dict(k_pages=0), -1),
+])
+def test_append_rejects_bad_descriptor(lib, kw, status):
+    d = _desc(**kw)
+    p = C.c_void_p(0x10)
+    rc = lib.kvq_quantize_append(C.byref(d), p, p, 1, 5, p, None, 1, None)
+    assert rc == status, lib.kvq_last_error()
+    assert lib.kvq_last_error()
+
+
+def test_append_argument_checks(lib):
+    d = _desc()
+    p = C.c_void_p(0x10)
+    assert lib.kvq_quantize_append(C.byref(d), p, p, 1, -1, p, None, 1, None) == -1
+    assert lib.kvq_quantize_append(C.byref(d), None, p, 1, 5, p, None, 1, None) == -1
+    assert lib.kvq_quantize_append(C.byref(d), p, p, 9, 5, p, None, 1, None) == -1
+    assert lib.kvq_quantize_append(C.byref(d), p, p, 1, 5, p, p, 0, None) == -2   # T dtype mismatch
+    assert lib.kvq_quantize_append(C.byref(d), p, p, 1, 0, p, None, 1, None) == 0  # nothing to do
+    assert lib.kvq_quantize_append(None, p, p, 1, 5, p, None, 1, None) == -1
+
+
+def test_decode_argument_checks(lib):
+    d = _desc()
+    p = C.c_void_p(0x10)
+    call = lambda **kw: lib.kvq_decode_attn(
+        C.byref(kw.get("d", d)), kw.get("q", p), kw.get("qd", 1), kw.get("B", 2), kw.get("Hq", 32),
+        None, kw.get("bt", p), kw.get("mp", 4), kw.get("sl", p), kw.get("msl", 256),
+        kw.get("scale", 0.088), kw.get("out", p), kw.get("ws", None), kw.get("wsb", 0), None)
+    assert call(Hq=30) == -1                    # not a multiple of the KV heads
+    assert call(Hq=8 * 17) == -2                # more than 16 query heads per KV head
+    assert call(mp=3) == -1                     # block table too short for max_seq_len
+    assert call(B=-1) == -1
+    assert call(B=0) == 0
+    assert call(q=None) == -1
+    assert call(qd=5) == -1
+    assert call(scale=float("inf")) == -1
+    need = lib.kvq_decode_workspace_bytes(C.byref(d), 64, 32, 16384)
+    assert need > 0
+    assert call(B=64, mp=256, msl=16384) == -3  # workspace missing
+    assert call(B=64, mp=256, msl=16384, ws=p, wsb=need - 1) == -3
+    assert lib.kvq_decode_workspace_bytes(C.byref(d), 1, 32, 0) == 0
+
+
+def test_dequant_argument_checks(lib):
+    d = _desc()
+    p = C.c_void_p(0x10)
+    assert lib.kvq_dequant(C.byref(d), 2, p, 5, p, None) == -1
+    assert lib.kvq_dequant(C.byref(d), 0, None, 5, p, None) == -1
+    assert lib.kvq_dequant(C.byref(d), 0, p, 0, p, None) == 0

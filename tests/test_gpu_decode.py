@@ -1,0 +1,185 @@
+"""GPU parity of the read path (kvq_decode_attn) against the CPU oracle, through the C ABI.
+
+Stage C: the oracle writes the packed cache (host), the same bytes are uploaded, and the
+         GPU decode must match the oracle's fp64 attention within 2e-3 max relative
+         error per (sequence, query head) row (max_j |o - r| / max_j |r|).
+Stage D: end to end -- GPU write path then GPU decode against oracle write path then
+         oracle decode, same bound.
+Full-size cases use the workloads' real shapes and compare a seeded sample of rows.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from decode_attention_kvq_amd import api, calib, synth
+from helpers import row_rel_err
+
+pytestmark = pytest.mark.gpu
+
+TOL = 2e-3
+TORCH_DT = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}
+
+
+def _transforms(config, H, G, dtype="bf16"):
+    ts, tis = [], []
+    for h in range(H):
+        kc, qc = synth.calibration_set(config, h, G)
+        t, ti = calib.calibrate_key_transform(kc, qc, store_bf16=(dtype == "bf16"))
+        ts.append(t)
+        tis.append(ti)
+    return np.stack(ts), np.stack(tis)
+
+
+def _gpu_decode(kp, vp, q, bt, seq, bits, tinv=None, q_dtype="f32", max_seq_len=None):
+    H = kp.shape[1]
+    cache = api.KVCache(kp.shape[0], H, bits[0], bits[1], k_pages=torch.from_numpy(kp).cuda(),
+                        v_pages=torch.from_numpy(vp).cuda())
+    qt = torch.from_numpy(q).to(TORCH_DT[q_dtype]).cuda()
+    msl = int(np.max(seq)) if max_seq_len is None else max_seq_len
+    out = api.kvq_decode_attn(cache, qt, torch.from_numpy(bt).cuda(), torch.from_numpy(seq).cuda(), msl,
+                              t_k_inv_t=None if tinv is None else torch.from_numpy(tinv).cuda())
+    torch.cuda.synchronize()
+    return out.cpu().numpy()
+
+
+def _oracle_cache(rng, B, H, seq, bits, config=1, t=None, quant=("percentile", "percentile"), extra_pages=3):
+    pps = max(1, int(-(-max(seq) // 64)))
+    num_pages = B * pps + extra_pages
+    kp = oracle.new_pool(num_pages, H, bits[0], rng=rng)
+    vp = oracle.new_pool(num_pages, H, bits[1], rng=rng)
+    bt = synth.shuffled_block_table(B, pps, num_pages, rng)
+    slots = synth.slots_for(bt, seq)
+    w = synth.Workload("t", config, H, H, 1, len(slots), bits[0], bits[1], quant[0], "bf16", True)
+    k, v = synth.kv_tokens(w, len(slots))
+    qm = {"percentile": oracle.PERCENTILE, "rms": oracle.RMS}
+    oracle.append(kp, vp, k, v, slots, t_k=t, bits_k=bits[0], bits_v=bits[1],
+                  quant_k=qm[quant[0]], quant_v=qm[quant[1]])
+    return kp, vp, bt
+
+
+@pytest.mark.parametrize("bits", [(2, 2), (4, 4), (2, 4), (4, 2)])
+@pytest.mark.parametrize("group", [1, 4, 8, 16])
+def test_stage_c_oracle_cache(bits, group):
+    rng = np.random.default_rng(100 + 10 * bits[0] + bits[1] + group)
+    B, H = 4, 2
+    seq = np.array([1, 63, 130, 700], np.int32)
+    t, tinv = _transforms(1, H, group)
+    kp, vp, bt = _oracle_cache(rng, B, H, seq, bits, t=t)
+    q = synth.decode_queries(synth.Workload("q", 1, H * group, H, B, 1, 2, 2, "percentile", "bf16", True))
+    got = _gpu_decode(kp, vp, q, bt, seq, bits, tinv=tinv, q_dtype="bf16")
+    ref = oracle.decode_attention(kp, vp, q, bt, seq, t_inv_t=tinv, bits_k=bits[0], bits_v=bits[1])
+    err = row_rel_err(got, ref)
+    assert err.max() <= TOL, (err.max(), np.unravel_index(err.argmax(), err.shape))
+
+
+@pytest.mark.parametrize("q_dtype", ["f32", "bf16", "f16"])
+def test_stage_c_random_codes_and_empty_sequences(q_dtype):
+    rng = np.random.default_rng(7)
+    B, H, G = 5, 3, 4
+    seq = np.array([0, 64, 65, 1000, 2], np.int32)
+    pps = 16
+    num_pages = B * pps
+    kp = synth.random_packed_pool(rng, num_pages, H, 2)
+    vp = synth.random_packed_pool(rng, num_pages, H, 4)
+    bt = synth.shuffled_block_table(B, pps, num_pages, rng)
+    q = synth.to_dtype(rng.standard_normal((B, H * G, 128)).astype(np.float32) * 3, q_dtype)
+    got = _gpu_decode(kp, vp, q, bt, seq, (2, 4), q_dtype=q_dtype, max_seq_len=1000)
+    ref = oracle.decode_attention(kp, vp, q, bt, seq, bits_k=2, bits_v=4)
+    assert np.all(got[0] == 0)
+    err = row_rel_err(got[1:], ref[1:])
+    assert err.max() <= TOL, err.max()
+
+
+def test_identity_inverse_equals_no_transform():
+    rng = np.random.default_rng(8)
+    B, H, G = 2, 2, 4
+    seq = np.array([300, 77], np.int32)
+    kp, vp, bt = _oracle_cache(rng, B, H, seq, (2, 2))
+    q = rng.standard_normal((B, H * G, 128)).astype(np.float32)
+    eye = np.broadcast_to(np.eye(128, dtype=np.float32), (H, 128, 128)).copy()
+    a = _gpu_decode(kp, vp, q, bt, seq, (2, 2), tinv=eye)
+    b = _gpu_decode(kp, vp, q, bt, seq, (2, 2), tinv=None)
+    assert np.array_equal(a, b)
+
+
+def test_split_kv_long_sequences():
+    """Sequences long enough to be split across several workgroups (combine kernel)."""
+    rng = np.random.default_rng(9)
+    B, H, G = 2, 2, 8
+    seq = np.array([5000, 3333], np.int32)
+    kp, vp, bt = _oracle_cache(rng, B, H, seq, (2, 2))
+    q = synth.decode_queries(synth.Workload("q", 2, H * G, H, B, 1, 2, 2, "percentile", "bf16", True))
+    cache = api.KVCache(kp.shape[0], H, 2, 2)
+    assert api.decode_workspace_bytes(cache, B, H * G, 5000) > 0
+    got = _gpu_decode(kp, vp, q, bt, seq, (2, 2), q_dtype="bf16")
+    ref = oracle.decode_attention(kp, vp, q, bt, seq, bits_k=2, bits_v=2)
+    assert row_rel_err(got, ref).max() <= TOL
+
+
+def test_stage_d_tiny_end_to_end():
+    """The tiny workload end to end: 256 fp32 tokens, 4-bit, fp32 transform, one query."""
+    w = synth.WORKLOADS["tiny"]
+    k, v = synth.kv_tokens(w, w.seq_len)
+    t, tinv = _transforms(0, 1, 1, dtype="f32")
+    q = synth.decode_queries(w)
+    slots = np.arange(w.seq_len, dtype=np.int64)
+    bt = np.arange(4, dtype=np.int32)[None]
+    seq = np.array([w.seq_len], np.int32)
+    cache = api.KVCache(4, 1, 4, 4)
+    api.kvq_quantize_append(cache, torch.from_numpy(k).cuda(), torch.from_numpy(v).cuda(),
+                            torch.from_numpy(slots).cuda(), t_k=torch.from_numpy(t).cuda())
+    out = api.kvq_decode_attn(cache, torch.from_numpy(q).cuda(), torch.from_numpy(bt).cuda(),
+                              torch.from_numpy(seq).cuda(), w.seq_len, t_k_inv_t=torch.from_numpy(tinv).cuda())
+    got = out.cpu().numpy()
+    kp, vp = oracle.new_pool(4, 1, 4), oracle.new_pool(4, 1, 4)
+    oracle.append(kp, vp, k, v, slots, t_k=t, bits_k=4, bits_v=4)
+    ref = oracle.decode_attention(kp, vp, q, bt, seq, t_inv_t=tinv, bits_k=4, bits_v=4)
+    assert row_rel_err(got, ref).max() <= TOL
+
+
+def test_qwen3_8b_b1_16k_full():
+    """Qwen3-8B-shaped layer, batch 1, 16384 cached tokens, 2-bit: stage C and stage D on
+    every row."""
+    w = synth.WORKLOADS["qwen3-8b-b1-16k"]
+    H, n = w.heads_kv, w.seq_len
+    t, tinv = _transforms(w.config, H, w.group)
+    k, v = synth.kv_tokens(w, n)
+    q = synth.decode_queries(w)
+    pages = n // 64
+    rng = np.random.default_rng(10)
+    bt = rng.permutation(pages).astype(np.int32)[None]
+    seq = np.array([n], np.int32)
+    slots = synth.slots_for(bt, seq)
+    kp, vp = oracle.new_pool(pages, H, 2), oracle.new_pool(pages, H, 2)
+    oracle.append(kp, vp, k, v, slots, t_k=t, bits_k=2, bits_v=2)
+    ref = oracle.decode_attention(kp, vp, q, bt, seq, t_inv_t=tinv, bits_k=2, bits_v=2)
+    got_c = _gpu_decode(kp, vp, q, bt, seq, (2, 2), tinv=tinv, q_dtype="bf16")
+    assert row_rel_err(got_c, ref).max() <= TOL
+    cache = api.KVCache(pages, H, 2, 2)
+    api.kvq_quantize_append(cache, torch.from_numpy(k).to(torch.bfloat16).cuda(),
+                            torch.from_numpy(v).to(torch.bfloat16).cuda(), torch.from_numpy(slots).cuda(),
+                            t_k=torch.from_numpy(t).to(torch.bfloat16).cuda())
+    out = api.kvq_decode_attn(cache, torch.from_numpy(q).to(torch.bfloat16).cuda(), torch.from_numpy(bt).cuda(),
+                              torch.from_numpy(seq).cuda(), n, t_k_inv_t=torch.from_numpy(tinv).cuda())
+    assert row_rel_err(out.cpu().numpy(), ref).max() <= TOL
+
+
+@pytest.mark.parametrize("name", ["qwen3-8b-b64-16k", "long-b16-128k-quest"])
+def test_full_size_decode_sampled(name):
+    """Full-size caches of random codes in the launch configuration the benchmark times;
+    the oracle recomputes a seeded sample of sequences (all their query heads)."""
+    w = synth.WORKLOADS[name]
+    rng = np.random.default_rng(11)
+    H, B, pps = w.heads_kv, w.batch, w.pages_per_seq
+    kp = synth.random_packed_pool(rng, B * pps, H, w.bits_k)
+    vp = synth.random_packed_pool(rng, B * pps, H, w.bits_v)
+    bt = synth.contiguous_block_table(B, pps)
+    seq = np.full(B, w.seq_len, np.int32)
+    q = synth.decode_queries(w)
+    _, tinv = _transforms(w.config, H, w.group)
+    got = _gpu_decode(kp, vp, q, bt, seq, (w.bits_k, w.bits_v), tinv=tinv, q_dtype="bf16")
+    for b in sorted(rng.choice(B, 2, replace=False)):
+        ref = oracle.decode_attention(kp, vp, q[b:b + 1], bt[b:b + 1], seq[b:b + 1], t_inv_t=tinv,
+                                      bits_k=w.bits_k, bits_v=w.bits_v)
+        assert row_rel_err(got[b:b + 1], ref).max() <= TOL, b
