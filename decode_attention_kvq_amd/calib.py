@@ -81,8 +81,8 @@ def calibrate_key_transform(k_cal: np.ndarray, q_cal: np.ndarray, gamma: float =
     T is what the write path applies (k' = k T); when store_bf16 it holds bf16 values.
     T_inv_T = (T^-1)^T of exactly that stored T, for the read path (q' = q T^-T)."""
     t = wush(*key_statistics(k_cal, q_cal), gamma=gamma, hadamard=hadamard)
-    t_store = round_bf16(t) if store_bf16 else t.astype(np.float32)
-    t_inv_t = np.linalg.inv(t_store.astype(np.float64)).T.astype(np.float32)
+    t_store = np.ascontiguousarray(round_bf16(t) if store_bf16 else t.astype(np.float32))
+    t_inv_t = np.ascontiguousarray(np.linalg.inv(t_store.astype(np.float64)).T, dtype=np.float32)
     return t_store, t_inv_t
 
 

@@ -210,8 +210,8 @@ __device__ __forceinline__ GroupQuant make_quant(float lo, float hi, int bits) {
   GroupQuant g;
   g.lmax = (float)((1 << bits) - 1);
   const float s = (hi - lo) / g.lmax;
-  g.s16 = f32_to_f16_bits(sat_f16(s));
-  g.z16 = f32_to_f16_bits(sat_f16(lo));
+  g.s16 = f32_to_f16_rne(sat_f16(s));
+  g.z16 = f32_to_f16_rne(sat_f16(lo));
   const float sf = f16_bits_to_f32(g.s16);
   g.zf = f16_bits_to_f32(g.z16);
   g.r = (sf == 0.0f) ? 0.0f : 1.0f / sf;

@@ -21,11 +21,31 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 __host__ __device__ constexpr int code_bytes(int bits) { return kPageTokens * kHeadDim * bits / 8; }
 __host__ __device__ constexpr int block_bytes(int bits) { return code_bytes(bits) + 4 * kPageTokens; }
 
-// fp32 <-> fp16 bit patterns.  The conversion rounds to nearest even (the default
-// rounding mode of the shader); fp16 subnormals are kept.
+// fp32 -> fp16 bits with the hardware conversion (operands of matrix-core products,
+// where the last rounding bit does not matter).
 __device__ __forceinline__ uint16_t f32_to_f16_bits(float x) {
   _Float16 h = (_Float16)x;
   return __builtin_bit_cast(uint16_t, h);
+}
+
+// fp32 -> fp16 bits, round to nearest with ties to even, in integer arithmetic from the
+// binary16 definition (1 sign, 5 exponent bits with bias 15, 10 fraction bits).  Used for
+// stored scales and zeros, which must round ties to even.  |x| >= 65520 gives infinity.
+__device__ __forceinline__ uint16_t f32_to_f16_rne(float x) {
+  const uint32_t u = __float_as_uint(x);
+  const uint32_t sign = (u >> 16) & 0x8000u;
+  const uint32_t a = u & 0x7FFFFFFFu;
+  if (a >= 0x7F800000u) return (uint16_t)(sign | (a > 0x7F800000u ? 0x7E00u : 0x7C00u));
+  if (a >= 0x477FF000u) return (uint16_t)(sign | 0x7C00u);
+  if (a < 0x38800000u) {
+    // below 2^-14 the fp16 spacing is 2^-24: scale exactly, round to an integer (RNE)
+    const float m = rintf(__uint_as_float(a) * 16777216.0f);
+    return (uint16_t)(sign | (uint32_t)m);
+  }
+  uint32_t h = (((a >> 23) - 112u) << 10) | ((a >> 13) & 0x3FFu);
+  const uint32_t rem = a & 0x1FFFu;
+  h += (rem > 0x1000u) || (rem == 0x1000u && (h & 1u));
+  return (uint16_t)(sign | h);
 }
 __device__ __forceinline__ float f16_bits_to_f32(uint32_t bits16) {
   return (float)__builtin_bit_cast(_Float16, (uint16_t)bits16);

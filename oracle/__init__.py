@@ -53,17 +53,17 @@ def lib():
         L.oracle_f32_to_f16_array.argtypes = [P, P, i64]
         L.oracle_f16_to_f32_array.argtypes = [P, P, i64]
         L.oracle_transform_keys.argtypes = [P, P, i64, i32, P]
-        L.oracle_percentile_position.argtypes = [f64, i32, P, P]
-        L.oracle_clip_percentile.argtypes = [P, i32, f64, f64, P, P]
+        L.oracle_percentile_position.argtypes = [f32, i32, P, P]
+        L.oracle_clip_percentile.argtypes = [P, i32, f32, f32, P, P]
         L.oracle_clip_rms.argtypes = [P, i32, f32, P, P]
         L.oracle_quantize_group.argtypes = [P, i32, i32, f32, f32, P, P, P]
-        L.oracle_quantize_rows.argtypes = [P, i64, i32, i32, f64, f64, f32, P, P, P, P, P]
+        L.oracle_quantize_rows.argtypes = [P, i64, i32, i32, f32, f32, f32, P, P, P, P, P]
         L.oracle_block_bytes.restype = i64
         L.oracle_block_bytes.argtypes = [i32]
         L.oracle_pack_token.argtypes = [P, i32, i32, i32, P, C.c_uint16, C.c_uint16]
         L.oracle_unpack_token.argtypes = [P, i32, i32, i32, P, P, P]
         L.oracle_append.restype = i32
-        L.oracle_append.argtypes = [P, P, i64, i32, i32, i32, i32, i32, f64, f64, f32, f32,
+        L.oracle_append.argtypes = [P, P, i64, i32, i32, i32, i32, i32, f32, f32, f32, f32,
                                     P, P, P, i64, P]
         L.oracle_dequant.argtypes = [P, i32, i32, i32, P, i64, P]
         L.oracle_decode_attention.argtypes = [P, P, i32, i32, i32, P, i32, i32, P, P, i32, P,
@@ -114,6 +114,7 @@ def transform_keys(k, t) -> np.ndarray:
 
 
 def percentile_position(p: float, n: int = HEAD_DIM):
+    """(i, f) for an fp32 percentile p: rank = fp64(p) * (n-1), f rounded to fp32."""
     i = C.c_int()
     f = C.c_float()
     lib().oracle_percentile_position(p, n, C.byref(i), C.byref(f))

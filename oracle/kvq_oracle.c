@@ -118,10 +118,11 @@ static int cmp_float(const void* a, const void* b)
 
 /* Percentile position for probability p over n sorted values: linear interpolation
    between order statistics at rank p*(n-1) (the common "linear" definition).
-   rank is formed in fp64; the fractional weight is rounded once to fp32. */
-void oracle_percentile_position(double p, int n, int* i_out, float* f_out)
+   p is an fp32 value (the type the cache descriptor carries); rank is formed in fp64
+   from it and the fractional weight is rounded once to fp32. */
+void oracle_percentile_position(float p, int n, int* i_out, float* f_out)
 {
-    double rank = p * (double)(n - 1);
+    double rank = (double)p * (double)(n - 1);
     int i = (int)floor(rank);
     if (i < 0) i = 0;
     float f = (float)(rank - (double)i);
@@ -132,7 +133,7 @@ void oracle_percentile_position(double p, int n, int* i_out, float* f_out)
 
 /* Interpolated order statistic: s[i] + f*(s[i+1]-s[i]) as one fused multiply-add
    in fp32, plus +0.0f so that a zero result is +0. */
-static float interpolate_sorted(const float* s, int n, double p)
+static float interpolate_sorted(const float* s, int n, float p)
 {
     int i; float f;
     oracle_percentile_position(p, n, &i, &f);
@@ -142,7 +143,7 @@ static float interpolate_sorted(const float* s, int n, double p)
 
 /* OSCAR-style percentile clip ([W] §5.3): lo/hi are the p_lo/p_hi percentiles of the
    group's values. */
-void oracle_clip_percentile(const float* x, int n, double p_lo, double p_hi, float* lo, float* hi)
+void oracle_clip_percentile(const float* x, int n, float p_lo, float p_hi, float* lo, float* hi)
 {
     float* s = (float*)malloc((size_t)n * sizeof(float));
     memcpy(s, x, (size_t)n * sizeof(float));
@@ -209,7 +210,7 @@ enum { ORACLE_PERCENTILE = 0, ORACLE_RMS = 1 };
 
 /* Clip + quantize each row of x [rows][128]. */
 void oracle_quantize_rows(const float* x, int64_t rows, int bits, int quantizer,
-                          double p_lo, double p_hi, float alpha,
+                          float p_lo, float p_hi, float alpha,
                           uint8_t* codes, uint16_t* scale_h, uint16_t* zero_h,
                           float* lo_out, float* hi_out)
 {
@@ -309,7 +310,7 @@ void oracle_unpack_token(const uint8_t* block, int which, int bits, int o, uint8
 /* ------------------------------------------------------------------------- */
 int oracle_append(uint8_t* k_pool, uint8_t* v_pool, int64_t num_pages, int kv_heads,
                   int bits_k, int bits_v, int quant_k, int quant_v,
-                  double p_lo, double p_hi, float alpha_k, float alpha_v,
+                  float p_lo, float p_hi, float alpha_k, float alpha_v,
                   const float* k, const float* v, const float* t_k,
                   int64_t n, const int64_t* slots)
 {

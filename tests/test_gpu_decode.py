@@ -13,7 +13,7 @@ import torch
 
 import oracle
 from decode_attention_kvq_amd import api, calib, synth
-from helpers import row_rel_err
+from helpers import f16_ulp_distance, pool_codes, row_rel_err
 
 pytestmark = pytest.mark.gpu
 
@@ -140,7 +140,13 @@ def test_stage_d_tiny_end_to_end():
 
 def test_qwen3_8b_b1_16k_full():
     """Qwen3-8B-shaped layer, batch 1, 16384 cached tokens, 2-bit: stage C and stage D on
-    every row."""
+    every row.
+
+    Stage D compares the two write paths code by code (values bit-exact, keys <= 1e-4
+    flipped codes from fp32 vs fp64 transform accumulation) and the two end-to-end
+    outputs at the scale of the cached values: over 16K near-uniformly weighted tokens
+    the output is ~1/sqrt(n) of the values, so one legitimately flipped code moves it by
+    ~s/n, which a max|o|-relative measure would amplify by sqrt(n)."""
     w = synth.WORKLOADS["qwen3-8b-b1-16k"]
     H, n = w.heads_kv, w.seq_len
     t, tinv = _transforms(w.config, H, w.group)
@@ -162,7 +168,17 @@ def test_qwen3_8b_b1_16k_full():
                             t_k=torch.from_numpy(t).to(torch.bfloat16).cuda())
     out = api.kvq_decode_attn(cache, torch.from_numpy(q).to(torch.bfloat16).cuda(), torch.from_numpy(bt).cuda(),
                               torch.from_numpy(seq).cuda(), n, t_k_inv_t=torch.from_numpy(tinv).cuda())
-    assert row_rel_err(out.cpu().numpy(), ref).max() <= TOL
+    assert np.array_equal(cache.v_pages.cpu().numpy(), vp)
+    gk = cache.k_pages.cpu().numpy()
+    sample = slots[:: 7]
+    gc, gs, gz = pool_codes(gk, 0, 2, sample)
+    oc, os_, oz = pool_codes(kp, 0, 2, sample)
+    assert np.mean(gc != oc) <= 1e-4, np.mean(gc != oc)
+    assert np.all(f16_ulp_distance(gs, os_) <= 1) and np.all(f16_ulp_distance(gz, oz) <= 1)
+    vmax = np.abs(oracle.dequant(vp, 1, 2, slots)).max(axis=0).max(axis=-1)      # [Hkv]
+    scale = np.repeat(vmax, w.group)[None]                                        # [1, Hq]
+    err = np.max(np.abs(out.cpu().numpy() - ref), axis=-1) / scale
+    assert err.max() <= TOL, err.max()
 
 
 @pytest.mark.parametrize("name", ["qwen3-8b-b64-16k", "long-b16-128k-quest"])

@@ -25,11 +25,13 @@ def _rows(n, seed, scale=1.0):
 
 
 def test_percentile_positions_worked_values(orc):
-    # rank = p*(n-1): 0.01*127 = 1.27 and 0.99*127 = 125.73
+    # rank = p*(n-1) with p the fp32 value: 0.01f*127 = 1.26999997..., 0.99f*127 = 125.73000...
     i, f = orc.percentile_position(0.01)
-    assert i == 1 and f == np.float32(0.27)
+    assert i == 1 and f == np.float32(float(np.float32(0.01)) * 127 - 1)
+    assert abs(f - 0.27) < 1e-7 and f != np.float32(0.27)
     i, f = orc.percentile_position(0.99)
-    assert i == 125 and f == np.float32(0.73)
+    assert i == 125 and f == np.float32(float(np.float32(0.99)) * 127 - 125)
+    assert abs(f - 0.73) < 2e-6
     assert orc.percentile_position(0.0) == (0, 0.0)
     assert orc.percentile_position(1.0) == (127, 0.0)
     assert orc.percentile_position(0.5) == (63, 0.5)
@@ -39,7 +41,9 @@ def test_percentile_positions_worked_values(orc):
 def test_percentile_matches_numpy(orc, p_lo, p_hi):
     x = _rows(2000, 7)
     _, _, _, lo, hi = orc.quantize_rows(x, 2, orc.PERCENTILE, p_lo, p_hi)
-    ref = np.percentile(x.astype(np.float64), [100 * p_lo, 100 * p_hi], axis=1, method="linear")
+    # the oracle's percentiles are fp32 values: hand numpy the same numbers
+    q = [100 * float(np.float32(p_lo)), 100 * float(np.float32(p_hi))]
+    ref = np.percentile(x.astype(np.float64), q, axis=1, method="linear")
     for got, r in ((lo, ref[0]), (hi, ref[1])):
         tol = 2 * _ulp(r) + 1e-30
         assert np.all(np.abs(got - r) <= tol), np.max(np.abs(got - r) / tol)
@@ -50,11 +54,15 @@ def test_percentile_order_statistics_brute_force(orc):
     _, _, _, lo, hi = orc.quantize_rows(x, 4, orc.PERCENTILE, 0.0, 1.0)
     assert np.array_equal(lo, x.min(axis=1) + np.float32(0))
     assert np.array_equal(hi, x.max(axis=1) + np.float32(0))
-    # p such that the rank is an integer: exactly the order statistic
-    s = np.sort(x, axis=1)
+    # p nearest to an integer rank: the order statistic itself, up to the few-ulp weight
+    # that fp32 p leaves on the next one (2/127 and 124/127 are not fp32 numbers)
+    s = np.sort(x, axis=1).astype(np.float64)
     _, _, _, lo, hi = orc.quantize_rows(x, 4, orc.PERCENTILE, 2 / 127, 124 / 127)
-    assert np.array_equal(lo, s[:, 2] + np.float32(0))
-    assert np.array_equal(hi, s[:, 124] + np.float32(0))
+    for got, k in ((lo, 2), (hi, 124)):
+        r = s[:, k]
+        gap = np.maximum(s[:, k + 1] - r, r - s[:, k - 1])
+        assert np.all(got >= s[:, k - 1]) and np.all(got <= s[:, k + 1])
+        assert np.all(np.abs(got - r) <= 4e-6 * gap + 2 * _ulp(r))
 
 
 def test_rms_clip_closed_form(orc):
