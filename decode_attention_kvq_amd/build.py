@@ -24,9 +24,15 @@ COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
           "-I", os.path.join(ROOT, "include"), "-I", CSRC]
 
 
+# The read path has no NaN semantics to honour (absent tokens are masked by selects), so
+# max/min need no canonicalisation; the write path keeps strict IEEE behaviour.
+# Matrix-core accumulators stay in ordinary VGPRs (no copies through AGPRs in the loop).
+EXTRA = {"kvq_decode.hip": ["-fno-honor-nans", "-mllvm", "-amdgpu-mfma-vgpr-form"]}
+
+
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC, *COMMON, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC, *COMMON, *EXTRA.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     noise = "'-packed-fp32-ops' is not a recognized feature"
     msg = "\n".join(l for l in (r.stdout + r.stderr).splitlines() if noise not in l)

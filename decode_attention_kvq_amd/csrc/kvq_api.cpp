@@ -64,13 +64,15 @@ kvq_status hip_status(hipError_t e) {
   return KVQ_ERR_HIP;
 }
 
+// Workspace: only when sequences are split over several workgroups, the partial outputs
+// and their (max, sum) pairs.
 struct WorkspaceLayout {
   size_t o_bytes, ml_bytes, total;
 };
 
 WorkspaceLayout workspace_layout(int batch, int heads_q, int chunks) {
   WorkspaceLayout w{0, 0, 0};
-  if (chunks <= 1 || batch <= 0) return w;
+  if (batch <= 0 || chunks <= 1) return w;
   const size_t rows = (size_t)batch * heads_q * chunks;
   w.o_bytes = (rows * 128 * sizeof(float) + 255) & ~(size_t)255;
   w.ml_bytes = (rows * 2 * sizeof(float) + 255) & ~(size_t)255;
@@ -159,13 +161,16 @@ kvq_status kvq_decode_attn(const kvq_cache_desc* cache, const void* q, kvq_dtype
   const WorkspaceLayout wl = workspace_layout(batch, num_q_heads, sp.chunks);
   if (wl.total > 0 && (!workspace || workspace_bytes < wl.total))
     return fail(KVQ_ERR_WORKSPACE, "workspace smaller than kvq_decode_workspace_bytes()");
+  if (cache->num_pages < 1) return fail(KVQ_ERR_INVALID_ARG, "num_pages must be >= 1");
   kvq::DecodeParams p{};
   p.kpool = static_cast<const uint8_t*>(cache->k_pages);
   p.vpool = static_cast<const uint8_t*>(cache->v_pages);
   p.q = q; p.tinv = t_k_inv_t; p.block_table = block_table; p.seq_lens = seq_lens; p.out = out;
-  p.ws_o = wl.total ? static_cast<float*>(workspace) : nullptr;
-  p.ws_ml = wl.total ? reinterpret_cast<float*>(static_cast<char*>(workspace) + wl.o_bytes) : nullptr;
+  char* ws = static_cast<char*>(workspace);
+  p.ws_o = wl.o_bytes ? reinterpret_cast<float*>(ws) : nullptr;
+  p.ws_ml = wl.ml_bytes ? reinterpret_cast<float*>(ws + wl.o_bytes) : nullptr;
   p.batch = batch; p.heads_q = num_q_heads; p.heads_kv = cache->num_kv_heads; p.group = group;
+  p.gpad = kvq::decode_group_pad(group);
   p.max_pages = max_pages; p.num_pages = cache->num_pages; p.pages_per_wave = sp.pages_per_wave; p.chunks = sp.chunks;
   p.score_scale = sm_scale * 1.4426950408889634f;
   return hip_status(kvq::launch_decode(p, cache->bits_k, cache->bits_v, (int)q_dtype,

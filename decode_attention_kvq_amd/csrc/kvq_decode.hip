@@ -6,24 +6,35 @@
 // Look" (NOVA-KV project page), "Three requirements": the cache is read on every step,
 // so per-element read work is paid over the whole cache.
 //
-// Design (gfx950, wave64).  Grid (chunk, KV head, sequence), 4 waves per workgroup; each
-// wave walks a contiguous run of pages with an online softmax, the workgroup merges its
-// four waves, and a second kernel merges chunks when a sequence is split.
-//
-// Both contractions run on the matrix cores as 16x16x32 fp16 products with fp32
-// accumulation, with the query heads of the group as the N = 16 columns:
-//   scores  S[token][head] = codes_K[token][ch] . q''[ch][head]
-//   output  O[ch][head]   += codes_V[ch][token] . P~[token][head]
+// One kernel (plus a merge when a sequence is split across workgroups): decode_kernel,
+// grid (chunk, KV head, sequence), 4 waves per workgroup.
+//  * Prologue: q' = q T^-T in fp32, scaled to log2 units, turned into the fp16
+//    matrix-core operand each lane holds.  Its loads go out before the first pages' copies
+//    so the arithmetic overlaps them.
+//  * Page walk: each wave walks a run of pages.  Pages are copied HBM -> LDS by the DMA
+//    path (global_load_lds, 16 B a lane, nontemporal) up to NBUF-1 pages ahead of the page
+//    in use, so several pages are in flight per wave without holding registers.
+// Both contractions run on 16x16x32 fp16 matrix cores with fp32 accumulation:
+//   scores  S[token][col] = codes_K[token][ch] . q''[ch][col]
+//   output  O[ch][col]   += codes_V[ch][token] . P~[token][col]
 // Codes are never converted arithmetically: an AND of the packed word with a mask
 // leaves, in each 16-bit half, one code at bit b*e of the mantissa of a subnormal fp16,
-// i.e. the exact value code * 2^(b*e) * 2^-24.  Codes in the top bits of a half are
-// shifted down first.  The factor 2^-(b*e) is folded into the other operand (q'' per
-// channel, P~ per token), so one AND yields two operands.  Scale and zero are applied
-// outside the products:
+// i.e. the exact value code * 2^(b*e) * 2^-24 (codes in the top bits of a half are
+// shifted down first).  The factor 2^-(b*e) is folded into the other operand.
+// Scale and zero are applied outside the products:
 //   score_t = s_t * (q . code_t) + z_t * sum(q)
 //   out     = (sum_t p_t s_t code_t + sum_t p_t z_t) / sum_t p_t
-// The token order inside a score tile is chosen so that each lane's score accumulators
-// hold exactly the tokens that lane feeds to the P.V product; no shuffles are needed.
+//
+// Column packing.  The 16 columns hold GP >= G query heads repeated in 16/GP blocks;
+// score tile b (16 tokens) only feeds the columns of block b % (16/GP), so one 16x16
+// accumulator holds 64 tokens x 4 heads at GP = 4 and every lane's softmax work is
+// useful.  A lane (column n = block * GP + head, lane group kg) holds the scores of
+// tokens 16*kg + 4*b + r of its tiles b, which are exactly the tokens it must feed to
+// the P.V product for column n: no data moves between lanes.  Each column keeps its
+// own running max, so the only cross-lane steps per page are over the four lane groups
+// of a column; columns of one head are merged once at the end.
+#include <type_traits>
+
 #include "kvq_device.h"
 #include "kvq_internal.h"
 
@@ -31,10 +42,8 @@ namespace kvq {
 namespace {
 
 constexpr int kWaves = 4;
-constexpr int kMaxGroup = 16;
 
 typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
-typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ half8 as_half8(u32x4 w) { return __builtin_bit_cast(half8, w); }
 
@@ -42,7 +51,6 @@ __device__ __forceinline__ half8 as_half8(u32x4 w) { return __builtin_bit_cast(h
 template <int B> __host__ __device__ constexpr int pair_class(int p) {
   return B == 2 ? (p <= 4 ? p : p - 5) : (p <= 1 ? p : p - 2);
 }
-template <int B> constexpr int num_classes() { return B == 2 ? 5 : 2; }
 
 // Two codes (pair p of word w: positions p and p + 16/b of the word) as two subnormal fp16.
 template <int B>
@@ -63,13 +71,31 @@ __device__ __forceinline__ uint32_t pack_f16x2(float a, float b) {
   return __builtin_bit_cast(uint32_t, h);
 }
 
-__device__ __forceinline__ float wave_max16(float v) {  // over lanes l, l^16, l^32, l^48
-  v = fmaxf(v, __shfl_xor(v, 16));
-  return fmaxf(v, __shfl_xor(v, 32));
+// Reductions over the four lane groups of a column (lanes l, l^16, l^32, l^48) with the
+// gfx950 row/half swaps: after a swap of a value with itself, the pair (dst, src) holds
+// the value of the lane and of its partner in some order, so max/sum of the pair is the
+// reduction over the partners.
+__device__ __forceinline__ float col_max(float v) {
+  const uint32_t u = __builtin_bit_cast(uint32_t, v);
+  auto a = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  v = fmaxf(__builtin_bit_cast(float, (uint32_t)a[0]), __builtin_bit_cast(float, (uint32_t)a[1]));
+  const uint32_t w = __builtin_bit_cast(uint32_t, v);
+  auto c = __builtin_amdgcn_permlane32_swap(w, w, false, false);
+  return fmaxf(__builtin_bit_cast(float, (uint32_t)c[0]), __builtin_bit_cast(float, (uint32_t)c[1]));
 }
-__device__ __forceinline__ float wave_sum16(float v) {
-  v += __shfl_xor(v, 16);
-  return v + __shfl_xor(v, 32);
+__device__ __forceinline__ int col_max_i(int v) {
+  auto a = __builtin_amdgcn_permlane16_swap((uint32_t)v, (uint32_t)v, false, false);
+  v = max((int)a[0], (int)a[1]);
+  auto c = __builtin_amdgcn_permlane32_swap((uint32_t)v, (uint32_t)v, false, false);
+  return max((int)c[0], (int)c[1]);
+}
+__device__ __forceinline__ float col_sum(float v) {
+  const uint32_t u = __builtin_bit_cast(uint32_t, v);
+  auto a = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  v = __builtin_bit_cast(float, (uint32_t)a[0]) + __builtin_bit_cast(float, (uint32_t)a[1]);
+  const uint32_t w = __builtin_bit_cast(uint32_t, v);
+  auto c = __builtin_amdgcn_permlane32_swap(w, w, false, false);
+  return __builtin_bit_cast(float, (uint32_t)c[0]) + __builtin_bit_cast(float, (uint32_t)c[1]);
 }
 
 // Channel of the K-code operand element j at K-step s for lane group kg.
@@ -92,47 +118,195 @@ template <int BV> __host__ __device__ constexpr int v_token_class(int u) {
   return BV == 2 ? pair_class<2>(u % 8) : pair_class<4>((u % 8) % 4);
 }
 
-template <int BK, int BV, typename TQ>
-__global__ __launch_bounds__(256) void decode_kernel(DecodeParams p) {
-  constexpr int kCodeBytesK = code_bytes(BK), kCodeBytesV = code_bytes(BV);
-  constexpr int NCV = num_classes<BV>();
-  const int chunk = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int G = p.group;
-  const int hq0 = kvh * G;
+// ---------------------------------------------------------------------------------
+// decode
+// ---------------------------------------------------------------------------------
+// Cache policy of the page loads: nontemporal.  Each cache byte is read once per step, so
+// keeping it in the caches only costs; streaming with this hint measured ~15% more
+// bandwidth than the default policy on the same access pattern.
+constexpr int kStreamPolicy = 2;   // gfx950 CPol NT bit
 
-  __shared__ float qs[kMaxGroup][kHeadDim];
-  __shared__ uint16_t qh[kMaxGroup][kHeadDim];
-  __shared__ float hconst[kMaxGroup][2];
-  __shared__ float red_o[kWaves][kMaxGroup][kHeadDim];
-  __shared__ float red_ml[kWaves][kMaxGroup][2];
+// Pages in flight per wave: a register ring of PIPE pages.
+template <int BK, int BV> constexpr int pipe_depth() { return BK + BV <= 4 ? 3 : 2; }
 
-  // ---- query compensation q' = q T^-T, scaled to log2 units ----
-  const TQ* qb = reinterpret_cast<const TQ*>(p.q) + ((int64_t)b * p.heads_q + hq0) * kHeadDim;
-  for (int idx = threadIdx.x; idx < G * kHeadDim; idx += 256) qs[idx / kHeadDim][idx % kHeadDim] = Elem<TQ>::get(qb, idx);
-  __syncthreads();
-  float qv[(kMaxGroup * kHeadDim) / 256];
-  {
-    const float* ti = p.tinv ? p.tinv + (int64_t)kvh * kHeadDim * kHeadDim : nullptr;
-    int r = 0;
-    for (int idx = threadIdx.x; idx < G * kHeadDim; idx += 256, ++r) {
-      const int g = idx / kHeadDim, j = idx % kHeadDim;
-      float acc = 0.0f;
-      if (ti) {
-        for (int c = 0; c < kHeadDim; ++c) acc = __builtin_fmaf(qs[g][c], ti[c * kHeadDim + j], acc);
-      } else {
-        acc = qs[g][j];
-      }
-      qv[r] = acc * p.score_scale;
-    }
-    __syncthreads();
-    r = 0;
-    for (int idx = threadIdx.x; idx < G * kHeadDim; idx += 256, ++r) qs[idx / kHeadDim][idx % kHeadDim] = qv[r];
-    __syncthreads();
+// A page's K and V blocks as seen by one lane, loaded straight into the registers the
+// matrix-core operands are built from.  A = accumulators (GP/4) of score rows per lane.
+template <int BK, int BV, int A> struct PageRegs {
+  typedef std::conditional_t<BK == 2, u32x2, u32x4> KRow;
+  KRow k[4];                   // K codes of tile t4: 32 channels of the lane's token
+  u32x4 v[BV == 2 ? 2 : 4];    // V codes: the lane's V row(s), two 16 B halves each
+  u32x2 meta[A][4];            // fp16 (s_k, z_k, s_v, z_v) of the lane's 4 tokens per row group
+};
+
+// Buffer resource of one 128-channel block: loads past num_records bytes return zero and
+// touch no memory, which is how a page that does not exist is "loaded".
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t block_rsrc(const uint8_t* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(base), (short)0, bytes, 0x00020000);
+}
+
+// Per-lane byte offsets inside a block (the same for every page).
+template <int BK, int BV, int A> struct LaneOffsets {
+  int k, v, meta[A];
+};
+
+template <int BK, int BV, int A>
+__device__ __forceinline__ void load_page(PageRegs<BK, BV, A>& r, __amdgpu_buffer_rsrc_t rk,
+                                          __amdgpu_buffer_rsrc_t rv, const LaneOffsets<BK, BV, A>& o) {
+#pragma unroll
+  for (int t4 = 0; t4 < 4; ++t4) {
+    if constexpr (BK == 2) r.k[t4] = __builtin_amdgcn_raw_buffer_load_b64(rk, o.k + 128 * t4, 0, kStreamPolicy);
+    else r.k[t4] = __builtin_amdgcn_raw_buffer_load_b128(rk, o.k + 256 * t4, 0, kStreamPolicy);
   }
+#pragma unroll
+  for (int rr = 0; rr < (BV == 2 ? 1 : 2); ++rr) {
+    r.v[2 * rr] = __builtin_amdgcn_raw_buffer_load_b128(rv, o.v + 512 * rr, 0, kStreamPolicy);
+    r.v[2 * rr + 1] = __builtin_amdgcn_raw_buffer_load_b128(rv, o.v + 512 * rr + 256, 0, kStreamPolicy);
+  }
+#pragma unroll
+  for (int a = 0; a < A; ++a) {
+    r.meta[a][0] = __builtin_amdgcn_raw_buffer_load_b64(rk, code_bytes(BK) + o.meta[a], 0, kStreamPolicy);
+    r.meta[a][1] = __builtin_amdgcn_raw_buffer_load_b64(rk, code_bytes(BK) + 128 + o.meta[a], 0, kStreamPolicy);
+    r.meta[a][2] = __builtin_amdgcn_raw_buffer_load_b64(rv, code_bytes(BV) + o.meta[a], 0, kStreamPolicy);
+    r.meta[a][3] = __builtin_amdgcn_raw_buffer_load_b64(rv, code_bytes(BV) + 128 + o.meta[a], 0, kStreamPolicy);
+  }
+}
+
+// Workgroup barrier for LDS traffic only: waits for this wave's LDS operations, not for
+// its outstanding global loads (the page loads in flight stay in flight).
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4) | (0 << 8));   // lgkmcnt(0) only
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// T^-T of a cache written without a key transform: the prologue always reads a matrix, so
+// its loads need no branch.
+struct IdentityMatrix {
+  float v[kHeadDim * kHeadDim];
+  constexpr IdentityMatrix() : v{} {
+    for (int i = 0; i < kHeadDim; ++i) v[i * (kHeadDim + 1)] = 1.0f;
+  }
+};
+__device__ constexpr IdentityMatrix kIdentity{};
+
+template <typename TQ, int BK, int BV, int GP>
+__global__ __launch_bounds__(256) void decode_kernel(DecodeParams p) {
+  constexpr int NB = 16 / GP;        // column blocks
+  constexpr int A = GP / 4;          // score accumulators (tiles per column)
+  constexpr int PIPE = pipe_depth<BK, BV>();
+  constexpr int KB = block_bytes(BK), VB = block_bytes(BV);
+  const int chunk = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const int kg = lane >> 4, n = lane & 15;
+  const int beta = n / GP;           // column block of this lane
+  const int G = p.group;
+
+  // merge buffers (per wave: 16 columns x 128 channels, then 16 x (m, l))
+  __shared__ __attribute__((aligned(16))) uint8_t smem[kWaves * 16 * (kHeadDim + 2) * 4];
+  // prologue scratch: q, then q'; the fp16 operand; two constants per head
+  __shared__ __attribute__((aligned(16))) float qs[GP * kHeadDim];
+  __shared__ __attribute__((aligned(16))) uint16_t qh[GP * kHeadDim];
+  __shared__ float hconst[GP * 2];
+
+  // ---- this wave's pages ----
+  const int nseq = min(p.seq_lens[b], p.max_pages * kPageTokens);
+  const int npages = (nseq + kPageTokens - 1) / kPageTokens;
+  const int wv = chunk * kWaves + wave;
+  const int pg0 = wv * p.pages_per_wave;
+  const int np = max(0, min(pg0 + p.pages_per_wave, npages) - pg0);
+  const int32_t* bt = p.block_table + (int64_t)b * p.max_pages;
+  // the wave's page ids (at most 64) sit one per lane; the walk reads them with readlane
+  int my_page = -1;                        // validated after the prologue loads are out
+  if (np > 0) my_page = bt[pg0 + min(lane, np - 1)];
+  auto page_id = [&](int i) -> int { return __builtin_amdgcn_readlane(my_page, i); };
+  // lane offsets inside a block: K tile t4 holds token 16*(n/4) + 4*t4 + n%4; the V rows
+  // are the lane group's; metadata of tokens 16*kg + 4*(a*NB + beta) + 0..3
+  LaneOffsets<BK, BV, A> lo;
+  {
+    const int tok0 = 16 * (n >> 2) + (n & 3);
+    lo.k = BK == 2 ? tok0 * 32 + kg * 8 : tok0 * 64 + kg * 16;
+    lo.v = (BV == 2 ? kg : 2 * kg) * kHeadDim * 4 + n * 16;
+#pragma unroll
+    for (int a = 0; a < A; ++a) lo.meta[a] = 2 * (16 * kg + 4 * (a * NB + beta));
+  }
+  // loads page i of the run (a page past the run or with an invalid id loads nothing)
+  auto load = [&](PageRegs<BK, BV, A>& r, int i) {
+    const int pid = i < np ? page_id(i) : -1;
+    const int64_t page = pid >= 0 ? pid : 0;
+    const int64_t blk = page * p.heads_kv + kvh;
+    load_page<BK, BV, A>(r, block_rsrc(p.kpool + blk * KB, pid >= 0 ? KB : 0),
+                         block_rsrc(p.vpool + blk * VB, pid >= 0 ? VB : 0), lo);
+  };
+
+  // ---- prologue: q' = q T^-T (fp32, log2 units), then the fp16 operand ----
+  // Loads of q and T^-T go out first, then the first pages' loads, so the arithmetic below
+  // overlaps the page fetch.
+  constexpr int QPER = GP * kHeadDim / 256;  // q elements per thread (GP >= G)
+  const TQ* qb = reinterpret_cast<const TQ*>(p.q) + ((int64_t)b * p.heads_q + (int64_t)kvh * G) * kHeadDim;
+  float qreg[QPER];
+#pragma unroll
+  for (int k = 0; k < QPER; ++k) {   // rows past the group read row 0 and are zeroed below
+    const int idx = (int)threadIdx.x + 256 * k;
+    qreg[k] = Elem<TQ>::get(qb, idx < G * kHeadDim ? idx : idx % kHeadDim);
+  }
+  // lane (quad, cgrp) of wave w: columns j0..j0+3 (j0 = 32w + 4 quad) of rows 16 cgrp..+15
+  const int quad = lane & 7, cgrp = lane >> 3;
+  const int j0 = 32 * wave + 4 * quad;
+  // both candidates live in global memory; saying so keeps these global (not flat) loads,
+  // whose completion the compiler counts precisely
+  typedef __attribute__((address_space(1))) const f32x4 gf32x4;
+  const gf32x4* tsrc = (const gf32x4*)(p.tinv ? p.tinv + (int64_t)kvh * kHeadDim * kHeadDim : kIdentity.v);
+  f32x4 trow[16];
+#pragma unroll
+  for (int cc = 0; cc < 16; ++cc) trow[cc] = tsrc[((16 * cgrp + cc) * kHeadDim + j0) / 4];
+  my_page = (lane < np && my_page >= 0 && my_page < p.num_pages) ? my_page : -1;
+  PageRegs<BK, BV, A> ring[PIPE];
+#pragma unroll
+  for (int d = 0; d < PIPE; ++d) load(ring[d], d);
+#pragma unroll
+  for (int k = 0; k < QPER; ++k)
+    qs[threadIdx.x + 256 * k] = (int)threadIdx.x + 256 * k < G * kHeadDim ? qreg[k] : 0.0f;
+  lds_barrier();
+  float qacc[GP][4];
+#pragma unroll
+  for (int g = 0; g < GP; ++g) {
+    float a4[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int cc = 0; cc < 16; cc += 4) {
+      const float4 qv = *reinterpret_cast<const float4*>(qs + g * kHeadDim + 16 * cgrp + cc);
+      const float qq[4] = {qv.x, qv.y, qv.z, qv.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) a4[k] = __builtin_fmaf(qq[e], trow[cc + e][k], a4[k]);
+      }
+    }
+    // sum over the 8 row groups (lane bits 3..5): xor 8 by a row rotation, then the swaps
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int u = __builtin_bit_cast(int, a4[k]);
+      const float v = a4[k] + __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(u, 0x128, 0xF, 0xF, false));
+      qacc[g][k] = col_sum(v);
+    }
+  }
+  lds_barrier();                           // every read of q is done: q' replaces it
+  if (cgrp == 0) {
+#pragma unroll
+    for (int g = 0; g < GP; ++g)
+      if (g < G) {
+        float4 o;
+        o.x = qacc[g][0] * p.score_scale;
+        o.y = qacc[g][1] * p.score_scale;
+        o.z = qacc[g][2] * p.score_scale;
+        o.w = qacc[g][3] * p.score_scale;
+        *reinterpret_cast<float4*>(qs + g * kHeadDim + j0) = o;
+      }
+  }
+  lds_barrier();
   // fp16 operand q''[c] = q'[c] * 2^(E - BK*e(c)), E per head so that max|q''| < 2^15
   for (int g = wave; g < G; g += kWaves) {
-    const float a0 = qs[g][lane], a1 = qs[g][lane + 64];
+    const float a0 = qs[g * kHeadDim + lane], a1 = qs[g * kHeadDim + lane + 64];
     float amax = fmaxf(fabsf(a0), fabsf(a1));
 #pragma unroll
     for (int d = 1; d < 64; d <<= 1) amax = fmaxf(amax, __shfl_xor(amax, d));
@@ -143,233 +317,259 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeParams p) {
       const int c = lane + 64 * k;
       const int sh = BK * k_channel_class<BK>(c);
       const uint16_t hbits = f32_to_f16_bits(ldexpf(k ? a1 : a0, E - sh));
-      qh[g][c] = hbits;
+      qh[g * kHeadDim + c] = hbits;
       qsum += ldexpf(f16_bits_to_f32(hbits), sh - E);
     }
 #pragma unroll
     for (int d = 1; d < 64; d <<= 1) qsum += __shfl_xor(qsum, d);
     if (lane == 0) {
-      hconst[g][0] = qsum;
-      hconst[g][1] = ldexpf(1.0f, 24 - E);
+      hconst[2 * g] = qsum;
+      hconst[2 * g + 1] = ldexpf(1.0f, 24 - E);
     }
   }
-  __syncthreads();
-
-  const int kg = lane >> 4, i16 = lane & 15;
-  const int g = i16;                       // head column of this lane
-  const bool gvalid = g < G;
-  u32x4 bq[4];
+  lds_barrier();
+  // B operand of K-step s for this lane (column n = head n % GP, lane group kg), masked per
+  // column block: block beta's operand is the lane's own, the others are zero
+  u32x4 bq[NB][4];
+  const int gq = n % GP;
 #pragma unroll
-  for (int s = 0; s < 4; ++s)
+  for (int s = 0; s < 4; ++s) {
+    u32x4 w;
 #pragma unroll
     for (int jj = 0; jj < 4; ++jj) {
-      const uint32_t lo = gvalid ? qh[g][k_channel<BK>(s, kg, 2 * jj)] : 0u;
-      const uint32_t hi = gvalid ? qh[g][k_channel<BK>(s, kg, 2 * jj + 1)] : 0u;
-      bq[s][jj] = lo | (hi << 16);
+      const uint32_t lo = gq < G ? qh[gq * kHeadDim + k_channel<BK>(s, kg, 2 * jj)] : 0u;
+      const uint32_t hi = gq < G ? qh[gq * kHeadDim + k_channel<BK>(s, kg, 2 * jj + 1)] : 0u;
+      w[jj] = lo | (hi << 16);
     }
-  const float F = gvalid ? hconst[g][1] : 1.0f;             // score = F * x'
-  const float qsf = gvalid ? hconst[g][0] / hconst[g][1] : 0.0f;
+#pragma unroll
+    for (int bb = 0; bb < NB; ++bb) bq[bb][s] = (beta == bb) ? w : u32x4{0u, 0u, 0u, 0u};
+  }
+  const float F = gq < G ? hconst[2 * gq + 1] : 1.0f;                  // score = F * x'
+  const float qsf = gq < G ? hconst[2 * gq] / hconst[2 * gq + 1] : 0.0f;
 
-  // ---- walk this wave's pages ----
-  const int n = min(p.seq_lens[b], p.max_pages * kPageTokens);
-  const int npages = (n + kPageTokens - 1) / kPageTokens;
-  const int wv = chunk * kWaves + wave;
-  const int pg0 = wv * p.pages_per_wave;
-  const int pg1 = min(pg0 + p.pages_per_wave, npages);
-
+  // per (accumulator a, row r): token u = 4*(a*NB + beta) + r of this lane group
   f32x4 acc_o[8];
 #pragma unroll
   for (int mt = 0; mt < 8; ++mt) acc_o[mt] = f32x4{};
-  float lsum[NCV], zacc[NCV];
+  float lsum[A][4], zacc[A][4], nb[A][4];
+  int vcls[A][4];                        // BV * class of each held token: P~ carries 2^(S - vcls)
 #pragma unroll
-  for (int e = 0; e < NCV; ++e) { lsum[e] = 0.0f; zacc[e] = 0.0f; }
-  float m = -__builtin_inff();   // running max of x' for this lane's head
-  int S = 30;                    // P~ = p * s_v * 2^(S - BV*e)
-
-  const int64_t kstride = (int64_t)block_bytes(BK), vstride = (int64_t)block_bytes(BV);
-  const int32_t* bt = p.block_table + (int64_t)b * p.max_pages;
-
-  for (int pg = pg0; pg < pg1; ++pg) {
-    const int64_t page = bt[pg];
-    if (page < 0 || page >= p.num_pages) continue;   // invalid page id: contributes nothing
-    const uint8_t* kb = p.kpool + (page * p.heads_kv + kvh) * kstride;
-    const uint8_t* vb = p.vpool + (page * p.heads_kv + kvh) * vstride;
-
-    // K codes for the four 16-token tiles
-    uint32_t kw[4][BK == 2 ? 2 : 4];
+  for (int a = 0; a < A; ++a)
 #pragma unroll
-    for (int b4 = 0; b4 < 4; ++b4) {
-      const int tok = 16 * (i16 >> 2) + 4 * b4 + (i16 & 3);
-      if constexpr (BK == 2) {
-        u32x2 w = *reinterpret_cast<const u32x2*>(kb + tok * 32 + kg * 8);
-        kw[b4][0] = w[0]; kw[b4][1] = w[1];
-      } else {
-        u32x4 w = *reinterpret_cast<const u32x4*>(kb + tok * 64 + kg * 16);
-        kw[b4][0] = w[0]; kw[b4][1] = w[1]; kw[b4][2] = w[2]; kw[b4][3] = w[3];
-      }
+    for (int r = 0; r < 4; ++r) {
+      lsum[a][r] = 0.0f;
+      zacc[a][r] = 0.0f;
+      nb[a][r] = 0.0f;
+      int e = 0;
+#pragma unroll
+      for (int bb = 0; bb < NB; ++bb)
+        if (beta == bb) e = v_token_class<BV>(4 * (a * NB + bb) + r);
+      vcls[a][r] = BV * e;
     }
-    // metadata of tokens 16kg .. 16kg+15 (two fp16 per word)
-    const u32x4* kmeta = reinterpret_cast<const u32x4*>(kb + kCodeBytesK);
-    const u32x4* vmeta = reinterpret_cast<const u32x4*>(vb + kCodeBytesV);
-    u32x4 sk0 = kmeta[2 * kg], sk1 = kmeta[2 * kg + 1];
-    u32x4 zk0 = kmeta[8 + 2 * kg], zk1 = kmeta[8 + 2 * kg + 1];
-    u32x4 sv0 = vmeta[2 * kg], sv1 = vmeta[2 * kg + 1];
-    u32x4 zv0 = vmeta[8 + 2 * kg], zv1 = vmeta[8 + 2 * kg + 1];
-    // V codes: word rows of this lane group's tokens, channels 4*i16.. and 64+4*i16..
-    u32x4 vw[BV == 2 ? 1 : 2][2];
+  // halves of the P.V operand words that carry this lane's tiles (see the P.V step)
+  uint32_t bmask[2];
 #pragma unroll
-    for (int r = 0; r < (BV == 2 ? 1 : 2); ++r) {
-      const int row = BV == 2 ? kg : 2 * kg + r;
-      const u32x4* vrow = reinterpret_cast<const u32x4*>(vb + row * kHeadDim * 4);
-      vw[r][0] = vrow[i16];
-      vw[r][1] = vrow[16 + i16];
-    }
-    auto word8 = [](const u32x4& a, const u32x4& c, int w) -> uint32_t { return w < 4 ? a[w] : c[w - 4]; };
+  for (int s = 0; s < 2; ++s) {
+    const int t_lo = v_token<BV>(s, 0) / 4, t_hi = v_token<BV>(s, 1) / 4;   // same for every jj
+    bmask[s] = ((t_lo % NB == beta) ? 0x0000FFFFu : 0u) | ((t_hi % NB == beta) ? 0xFFFF0000u : 0u);
+  }
+  float m = -__builtin_inff();   // running max of x' for this lane's column
+  int S = 30;
 
-    // ---- scores ----
-    float x[16];
+  // ---- page walk: compute page i from ring slot i % PIPE, then refill the slot ----
+  auto compute = [&](const PageRegs<BK, BV, A>& pr, int i) {
+    const int valid_tokens = nseq - (pg0 + i) * kPageTokens;   // >= 1
+    const bool partial = valid_tokens < kPageTokens;
+
+    // ---- scores: tile t4 = tokens 16*(n/4) + 4*t4 + n%4 in rows n ----
+    f32x4 sacc[A];
 #pragma unroll
-    for (int b4 = 0; b4 < 4; ++b4) {
-      f32x4 acc = f32x4{};
+    for (int a = 0; a < A; ++a) sacc[a] = f32x4{};
+#pragma unroll
+    for (int t4 = 0; t4 < 4; ++t4) {
+      uint32_t kw[BK == 2 ? 2 : 4];
+#pragma unroll
+      for (int e = 0; e < (BK == 2 ? 2 : 4); ++e) kw[e] = pr.k[t4][e];
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
-        const uint32_t w = BK == 2 ? kw[b4][s / 2] : kw[b4][s];
+        const uint32_t w = BK == 2 ? kw[s / 2] : kw[s];
         const uint32_t ws = shifted<BK>(w);
-        u32x4 a;
+        u32x4 av;
 #pragma unroll
-        for (int jj = 0; jj < 4; ++jj) a[jj] = code_pair<BK>(w, ws, BK == 2 ? 4 * (s % 2) + jj : jj);
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(a), as_half8(bq[s]), acc, 0, 0, 0);
+        for (int jj = 0; jj < 4; ++jj) av[jj] = code_pair<BK>(w, ws, BK == 2 ? 4 * (s % 2) + jj : jj);
+        sacc[t4 / NB] = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(av), as_half8(bq[t4 % NB][s]),
+                                                              sacc[t4 / NB], 0, 0, 0);
       }
+    }
+    // metadata of the lane's tokens (4 consecutive per tile: 8 bytes each)
+    float x[A][4], sv[A][4], zv[A][4];
+#pragma unroll
+    for (int a = 0; a < A; ++a) {
+      const u32x2 skw = pr.meta[a][0], zkw = pr.meta[a][1], svw = pr.meta[a][2], zvw = pr.meta[a][3];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int u = 4 * b4 + r;
-        const uint32_t skw = word8(sk0, sk1, u / 2), zkw = word8(zk0, zk1, u / 2);
-        const float sk = (u & 1) ? hi_f16(skw) : lo_f16(skw);
-        const float zk = (u & 1) ? hi_f16(zkw) : lo_f16(zkw);
-        x[u] = __builtin_fmaf(acc[r], sk, zk * qsf);
+        const float sk = (r & 1) ? hi_f16(skw[r >> 1]) : lo_f16(skw[r >> 1]);
+        const float zk = (r & 1) ? hi_f16(zkw[r >> 1]) : lo_f16(zkw[r >> 1]);
+        sv[a][r] = (r & 1) ? hi_f16(svw[r >> 1]) : lo_f16(svw[r >> 1]);
+        zv[a][r] = (r & 1) ? hi_f16(zvw[r >> 1]) : lo_f16(zvw[r >> 1]);
+        x[a][r] = __builtin_fmaf(sacc[a][r], sk, zk * qsf);
       }
     }
-    const int valid_tokens = n - pg * kPageTokens;   // >= 1
-    const bool partial = valid_tokens < kPageTokens;
-    if (partial) {
+    if (partial) {                          // absent tokens: no weight, no garbage scale
 #pragma unroll
-      for (int u = 0; u < 16; ++u) x[u] = (16 * kg + u < valid_tokens) ? x[u] : -__builtin_inff();
+      for (int a = 0; a < A; ++a)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const bool ok = 16 * kg + 4 * (a * NB + beta) + r < valid_tokens;
+          x[a][r] = ok ? x[a][r] : -__builtin_inff();
+          sv[a][r] = ok ? sv[a][r] : 0.0f;
+          zv[a][r] = ok ? zv[a][r] : 0.0f;
+        }
     }
-
-    // ---- online softmax ----
-    float mx = x[0];
+    // ---- online softmax, per column ----
+    float mx = x[0][0];
+    float svm = sv[0][0];
 #pragma unroll
-    for (int u = 1; u < 16; ++u) mx = fmaxf(mx, x[u]);
-    mx = wave_max16(mx);
-    u16x2 svm = __builtin_bit_cast(u16x2, sv0[0]);
+    for (int a = 0; a < A; ++a)
 #pragma unroll
-    for (int w = 1; w < 8; ++w) svm = __builtin_elementwise_max(svm, __builtin_bit_cast(u16x2, word8(sv0, sv1, w)));
-    int svmax = max((int)svm[0], (int)svm[1]);
-    if (partial) {
-      svmax = 0;
-      for (int u = 0; u < 16; ++u) {
-        const uint32_t svw = word8(sv0, sv1, u / 2);
-        const int bits16 = (u & 1) ? (int)(svw >> 16) : (int)(svw & 0xFFFFu);
-        svmax = (16 * kg + u < valid_tokens) ? max(svmax, bits16) : svmax;
+      for (int r = 0; r < 4; ++r) {
+        mx = fmaxf(mx, x[a][r]);
+        svm = fmaxf(svm, sv[a][r]);
       }
-    }
-    svmax = max(svmax, __shfl_xor(svmax, 16));
-    svmax = max(svmax, __shfl_xor(svmax, 32));
-    const int s_page = svmax >= 0x400 ? 14 - ((svmax >> 10) - 15) : 29;
-    const int S_new = min(S, s_page);
+    mx = col_max(mx);
+    // the largest value scale of the column's tokens sets S: P~ < 2^15 keeps fp16 finite
+    const int svbits = col_max_i((int)__builtin_bit_cast(uint32_t, svm));   // sv >= 0
+    const int ev = svbits > 0 ? ((svbits >> 23) & 0xFF) - 127 : -30;
+    const int S_new = min(S, 14 - ev);
     const float m_new = fmaxf(m, mx);
     if (__any(m_new > m || S_new != S)) {
       const float alpha = exp2f(F * (m - m_new) + (float)(S_new - S));
 #pragma unroll
       for (int mt = 0; mt < 8; ++mt) acc_o[mt] *= alpha;
 #pragma unroll
-      for (int e = 0; e < NCV; ++e) { lsum[e] *= alpha; zacc[e] *= alpha; }
+      for (int a = 0; a < A; ++a)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          lsum[a][r] *= alpha;
+          zacc[a][r] *= alpha;
+          nb[a][r] = (float)(S_new - vcls[a][r]) - F * m_new;
+        }
       m = m_new;
       S = S_new;
     }
-    float nb[NCV];
+    float pt[A][4];
 #pragma unroll
-    for (int e = 0; e < NCV; ++e) nb[e] = (float)(S - BV * e) - F * m;
-    float pt[16];
+    for (int a = 0; a < A; ++a)
 #pragma unroll
-    for (int u = 0; u < 16; ++u) {
-      const int e = v_token_class<BV>(u);
-      const float pe = __builtin_amdgcn_exp2f(__builtin_fmaf(F, x[u], nb[e]));
-      const uint32_t svw = word8(sv0, sv1, u / 2), zvw = word8(zv0, zv1, u / 2);
-      const float sv = (u & 1) ? hi_f16(svw) : lo_f16(svw);
-      const float zv = (u & 1) ? hi_f16(zvw) : lo_f16(zvw);
-      if (partial && !(16 * kg + u < valid_tokens)) {
-        pt[u] = 0.0f;
-      } else {
-        lsum[e] += pe;
-        zacc[e] = __builtin_fmaf(pe, zv, zacc[e]);
-        pt[u] = pe * sv;
+      for (int r = 0; r < 4; ++r) {
+        const float pe = __builtin_amdgcn_exp2f(__builtin_fmaf(F, x[a][r], nb[a][r]));
+        lsum[a][r] += pe;
+        zacc[a][r] = __builtin_fmaf(pe, zv[a][r], zacc[a][r]);
+        pt[a][r] = pe * sv[a][r];
       }
-    }
 
-    // ---- P.V ----
+    // ---- P.V: B operand element (s, 2*jj + h) is token u = v_token(s, 2jj+h), i.e. tile
+    // b(s, h) = u/4, row jj; the lane feeds only its own tiles, the rest of the operand is 0
     u32x4 bp[2];
 #pragma unroll
     for (int s = 0; s < 2; ++s)
 #pragma unroll
-      for (int jj = 0; jj < 4; ++jj) bp[s][jj] = pack_f16x2(pt[v_token<BV>(s, 2 * jj)], pt[v_token<BV>(s, 2 * jj + 1)]);
+      for (int jj = 0; jj < 4; ++jj) {
+        const int t_lo = v_token<BV>(s, 2 * jj) / 4, t_hi = v_token<BV>(s, 2 * jj + 1) / 4;
+        if constexpr (NB == 1) {
+          bp[s][jj] = pack_f16x2(pt[t_lo][jj], pt[t_hi][jj]);
+        } else {
+          // both halves take the held value; a per-lane mask keeps the halves whose tile
+          // is this lane's (tile % NB == beta)
+          const uint32_t both = pack_f16x2(pt[t_lo / NB][jj], pt[t_hi / NB][jj]);
+          bp[s][jj] = both & bmask[s];
+        }
+      }
 #pragma unroll
-    for (int mt = 0; mt < 8; ++mt) {
+    for (int rr = 0; rr < (BV == 2 ? 1 : 2); ++rr) {
+      const u32x4 va = pr.v[2 * rr], vc = pr.v[2 * rr + 1];
 #pragma unroll
-      for (int s = 0; s < 2; ++s) {
-        const uint32_t w = BV == 2 ? vw[0][mt >> 2][mt & 3] : vw[s][mt >> 2][mt & 3];
-        const uint32_t ws = shifted<BV>(w);
-        u32x4 a;
+      for (int mt = 0; mt < 8; ++mt) {
 #pragma unroll
-        for (int jj = 0; jj < 4; ++jj) a[jj] = code_pair<BV>(w, ws, BV == 2 ? 4 * s + jj : jj);
-        acc_o[mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(a), as_half8(bp[s]), acc_o[mt], 0, 0, 0);
+        for (int s = 0; s < 2; ++s) {
+          if (BV == 4 && s != rr) continue;
+          const uint32_t w = (mt >> 2) ? vc[mt & 3] : va[mt & 3];
+          const uint32_t ws = shifted<BV>(w);
+          u32x4 av;
+#pragma unroll
+          for (int jj = 0; jj < 4; ++jj) av[jj] = code_pair<BV>(w, ws, BV == 2 ? 4 * s + jj : jj);
+          acc_o[mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(av), as_half8(bp[s]), acc_o[mt], 0, 0, 0);
+        }
       }
     }
+  };
+  // whole groups of PIPE pages (every path through an iteration issues the same loads, so
+  // the compiler's wait for each slot covers that slot's loads only), then the tail
+  int i0 = 0;
+  for (; i0 + PIPE <= np; i0 += PIPE) {
+#pragma unroll
+    for (int d = 0; d < PIPE; ++d) {
+      if (page_id(i0 + d) >= 0) compute(ring[d], i0 + d);   // an invalid page id contributes nothing
+      load(ring[d], i0 + d + PIPE);
+    }
   }
+#pragma unroll
+  for (int d = 0; d < PIPE - 1; ++d)
+    if (i0 + d < np && page_id(i0 + d) >= 0) compute(ring[d], i0 + d);
 
-  // ---- wave result: m (log2 units), l, o_num = acc * 2^(24-S) + z ----
+  // ---- column result: m (log2 units), l, o_num = acc * 2^(24-S) + z ----
   float l = 0.0f, z = 0.0f;
 #pragma unroll
-  for (int e = 0; e < NCV; ++e) {
-    l += ldexpf(lsum[e], BV * e - S);
-    z += ldexpf(zacc[e], BV * e - S);
-  }
-  l = wave_sum16(l);
-  z = wave_sum16(z);
-  const float mlog2 = (pg1 > pg0) ? F * m : -__builtin_inff();
-  const float oscale = ldexpf(1.0f, 24 - S);
-  if (gvalid) {
+  for (int a = 0; a < A; ++a)
 #pragma unroll
-    for (int mt = 0; mt < 8; ++mt)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int ch = 4 * (4 * kg + r) + (mt & 3) + 64 * (mt >> 2);
-        red_o[wave][g][ch] = __builtin_fmaf(acc_o[mt][r], oscale, z);
-      }
-    if (kg == 0) {
-      red_ml[wave][g][0] = mlog2;
-      red_ml[wave][g][1] = (pg1 > pg0) ? l : 0.0f;
+    for (int r = 0; r < 4; ++r) {
+      l += ldexpf(lsum[a][r], vcls[a][r] - S);
+      z += ldexpf(zacc[a][r], vcls[a][r] - S);
     }
+  l = col_sum(l);
+  z = col_sum(z);
+  const bool any_page = m != -__builtin_inff();
+  const float mlog2 = any_page ? F * m : -__builtin_inff();
+  const float oscale = ldexpf(1.0f, 24 - S);
+  __syncthreads();
+  float (*red_o)[16][kHeadDim] = reinterpret_cast<float (*)[16][kHeadDim]>(smem);
+  float (*red_ml)[16][2] = reinterpret_cast<float (*)[16][2]>(smem + kWaves * 16 * kHeadDim * 4);
+#pragma unroll
+  for (int mt = 0; mt < 8; ++mt)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int ch = 4 * (4 * kg + r) + (mt & 3) + 64 * (mt >> 2);
+      red_o[wave][n][ch] = __builtin_fmaf(acc_o[mt][r], oscale, z);
+    }
+  if (kg == 0) {
+    red_ml[wave][n][0] = mlog2;
+    red_ml[wave][n][1] = any_page ? l : 0.0f;
   }
   __syncthreads();
 
-  // ---- merge the four waves; write the result or the chunk partial ----
+  // ---- merge the waves and the column blocks of each head ----
+  const int hq0 = kvh * G;
   for (int idx = threadIdx.x; idx < G * kHeadDim; idx += 256) {
     const int gg = idx / kHeadDim, ch = idx % kHeadDim;
     float M = -__builtin_inff();
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, red_ml[w][gg][0]);
+    for (int w = 0; w < kWaves; ++w)
+#pragma unroll
+      for (int bb = 0; bb < NB; ++bb) M = fmaxf(M, red_ml[w][bb * GP + gg][0]);
     float L = 0.0f, O = 0.0f;
     if (M != -__builtin_inff()) {
 #pragma unroll
-      for (int w = 0; w < kWaves; ++w) {
-        const float mw = red_ml[w][gg][0];
-        if (mw != -__builtin_inff()) {
-          const float f = exp2f(mw - M);
-          L = __builtin_fmaf(red_ml[w][gg][1], f, L);
-          O = __builtin_fmaf(red_o[w][gg][ch], f, O);
+      for (int w = 0; w < kWaves; ++w)
+#pragma unroll
+        for (int bb = 0; bb < NB; ++bb) {
+          const int col = bb * GP + gg;
+          const float mw = red_ml[w][col][0];
+          if (mw != -__builtin_inff()) {
+            const float f = exp2f(mw - M);
+            L = __builtin_fmaf(red_ml[w][col][1], f, L);
+            O = __builtin_fmaf(red_o[w][col][ch], f, O);
+          }
         }
-      }
     }
     const int hq = hq0 + gg;
     if (p.chunks == 1) {
@@ -405,14 +605,13 @@ __global__ __launch_bounds__(128) void combine_kernel(DecodeParams p) {
   p.out[row * kHeadDim + ch] = L > 0.0f ? O / L : 0.0f;
 }
 
-template <int BK, int BV>
-hipError_t launch_bits(const DecodeParams& p, int q_dtype, hipStream_t stream) {
-  dim3 grid((unsigned)p.chunks, (unsigned)p.heads_kv, (unsigned)p.batch);
-  dim3 block(256);
-  switch (q_dtype) {
-    case 0: hipLaunchKernelGGL((decode_kernel<BK, BV, float>), grid, block, 0, stream, p); break;
-    case 1: hipLaunchKernelGGL((decode_kernel<BK, BV, __bf16>), grid, block, 0, stream, p); break;
-    default: hipLaunchKernelGGL((decode_kernel<BK, BV, _Float16>), grid, block, 0, stream, p); break;
+template <typename TQ, int BK, int BV>
+hipError_t launch_typed(const DecodeParams& p, hipStream_t stream) {
+  const dim3 grid((unsigned)p.chunks, (unsigned)p.heads_kv, (unsigned)p.batch);
+  switch (p.gpad) {
+    case 4: hipLaunchKernelGGL((decode_kernel<TQ, BK, BV, 4>), grid, dim3(256), 0, stream, p); break;
+    case 8: hipLaunchKernelGGL((decode_kernel<TQ, BK, BV, 8>), grid, dim3(256), 0, stream, p); break;
+    default: hipLaunchKernelGGL((decode_kernel<TQ, BK, BV, 16>), grid, dim3(256), 0, stream, p); break;
   }
   hipError_t err = hipGetLastError();
   if (err != hipSuccess || p.chunks == 1) return err;
@@ -420,15 +619,27 @@ hipError_t launch_bits(const DecodeParams& p, int q_dtype, hipStream_t stream) {
   return hipGetLastError();
 }
 
+template <int BK, int BV>
+hipError_t launch_bits(const DecodeParams& p, int q_dtype, hipStream_t stream) {
+  switch (q_dtype) {
+    case 0: return launch_typed<float, BK, BV>(p, stream);
+    case 1: return launch_typed<__bf16, BK, BV>(p, stream);
+    default: return launch_typed<_Float16, BK, BV>(p, stream);
+  }
+}
+
 }  // namespace
+
+int decode_group_pad(int group) { return group <= 4 ? 4 : (group <= 8 ? 8 : 16); }
 
 DecodeSplit decode_split(int batch, int heads_kv, int max_seq_len) {
   const int pages = (max_seq_len + kPageTokens - 1) / kPageTokens;
   const int64_t units = (int64_t)batch * heads_kv;
-  // about 8192 waves in flight over the chip, at least 4 pages per wave
-  int64_t ppw = (units * pages + 8191) / 8192;
+  // about 2048 waves (one resident round of 8 waves per CU), 4 to 64 pages per wave (a
+  // wave's page ids fit one register, one per lane)
+  int64_t ppw = (units * pages + 2047) / 2048;
   if (ppw < 4) ppw = 4;
-  if (ppw > 256) ppw = 256;
+  if (ppw > 64) ppw = 64;
   const int64_t waves = pages > 0 ? (pages + ppw - 1) / ppw : 1;
   DecodeSplit s;
   s.pages_per_wave = (int)ppw;

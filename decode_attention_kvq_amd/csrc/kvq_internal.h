@@ -34,6 +34,7 @@ struct DecodeParams {
   float* ws_o;            // [B][Hq][chunks][128]
   float* ws_ml;           // [B][Hq][chunks][2]
   int batch, heads_q, heads_kv, group;
+  int gpad;               // query heads per KV head rounded up to 4, 8 or 16
   int max_pages;          // row stride of block_table
   int64_t num_pages;      // pages in each pool (page ids outside are skipped)
   int pages_per_wave;
@@ -64,5 +65,6 @@ struct DecodeSplit {
   int chunks;
 };
 DecodeSplit decode_split(int batch, int heads_kv, int max_seq_len);
+int decode_group_pad(int group);
 
 }  // namespace kvq

@@ -111,7 +111,9 @@ kvq_status kvq_quantize_append(const kvq_cache_desc* cache, const void* k, const
                                const int64_t* slot_mapping, const void* t_k,
                                kvq_dtype t_dtype, void* stream);
 
-/* Workspace bytes kvq_decode_attn needs for these sizes (0 when none is needed). */
+/* Workspace bytes kvq_decode_attn needs for these sizes.  Non-zero only when the sizes
+ * make the launch split each sequence over several workgroups (few sequences, long
+ * contexts): the workspace then holds the partial outputs that a merge step combines. */
 size_t kvq_decode_workspace_bytes(const kvq_cache_desc* cache, int32_t batch,
                                   int32_t num_q_heads, int32_t max_seq_len);
 
@@ -130,7 +132,9 @@ size_t kvq_decode_workspace_bytes(const kvq_cache_desc* cache, int32_t batch,
  *   sm_scale     softmax scale (1/sqrt(128) for standard attention).
  *   out          device, [batch][num_q_heads][128] fp32, in the transformed value basis;
  *                an empty sequence gives zeros.
- *   workspace    device scratch of at least kvq_decode_workspace_bytes(...) bytes. */
+ *   workspace    device scratch of at least kvq_decode_workspace_bytes(...) bytes (may be
+ *                NULL when that is 0); its content on entry does not matter.  Calls that
+ *                share a workspace must be ordered (same stream). */
 kvq_status kvq_decode_attn(const kvq_cache_desc* cache, const void* q, kvq_dtype q_dtype,
                            int32_t batch, int32_t num_q_heads, const float* t_k_inv_t,
                            const int32_t* block_table, int32_t max_pages,

@@ -114,11 +114,17 @@ def test_decode_argument_checks(lib):
     assert call(q=None) == -1
     assert call(qd=5) == -1
     assert call(scale=float("inf")) == -1
-    need = lib.kvq_decode_workspace_bytes(C.byref(d), 64, 32, 16384)
-    assert need > 0
-    assert call(B=64, mp=256, msl=16384) == -3  # workspace missing
-    assert call(B=64, mp=256, msl=16384, ws=p, wsb=need - 1) == -3
+    # one long sequence is split over several workgroups: partial results need a workspace
+    need = lib.kvq_decode_workspace_bytes(C.byref(d), 1, 32, 16384)
+    assert need >= 32 * 2 * 130 * 4
+    assert call(B=1, mp=256, msl=16384) == -3  # workspace missing
+    assert call(B=1, mp=256, msl=16384, ws=p, wsb=need - 1) == -3
+    assert lib.kvq_decode_workspace_bytes(C.byref(d), 0, 32, 0) == 0
+    # many sequences fill the GPU without splitting: no workspace
+    assert lib.kvq_decode_workspace_bytes(C.byref(d), 64, 32, 16384) == 0
     assert lib.kvq_decode_workspace_bytes(C.byref(d), 1, 32, 0) == 0
+    d0 = _desc(num_pages=0)
+    assert call(d=d0) == -1                                                   # empty pool
 
 
 def test_dequant_argument_checks(lib):
