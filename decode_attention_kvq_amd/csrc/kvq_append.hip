@@ -23,9 +23,10 @@
 //   * rms clip: in-lane pairwise tree over the half, one exchange, correctly rounded
 //     sqrt.
 //   * keys: each lane writes its half of the token's row (16 or 32 bytes).
-//   * values: when the wave's 32 tokens fill an aligned run of one page, codes are
-//     transposed through LDS and whole words are stored; otherwise each code is
-//     merged into its word with atomic AND/OR so other tokens' bits survive.
+//   * values: codes are transposed through LDS; when the wave's 32 tokens fill an
+//     aligned run of one page, whole words are stored; otherwise the wave merges one
+//     token at a time into its words with atomic AND/OR (contiguous words per
+//     instruction), so other tokens' bits survive.
 #include "kvq_device.h"
 #include "kvq_internal.h"
 
@@ -89,10 +90,24 @@ __device__ __forceinline__ void load_half_row(const TIn* src, float (&x)[64]) {
   }
 }
 
-// k' = k . T on the matrix cores for the wave's 32 tokens.  tok_row: this lane's token
-// row (128 elements of the head).  tt: T^T of the head in LDS.
+// 64 16-bit elements held as 8 x 16 B (already loaded) as fp32.
 template <typename TIn>
-__device__ __forceinline__ void transform_mfma(const TIn* tok_row, const uint16_t* tt, int lane,
+__device__ __forceinline__ void unpack_half_row(const u32x4 (&raw)[8], float (&x)[64]) {
+  constexpr bool bf = __is_same(TIn, __bf16);
+#pragma unroll
+  for (int q = 0; q < 8; ++q)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      x[8 * q + 2 * e] = half_lo_to_f32(raw[q][e], bf);
+      x[8 * q + 2 * e + 1] = half_hi_to_f32(raw[q][e], bf);
+    }
+}
+
+// k' = k . T on the matrix cores for the wave's 32 tokens.  kop[ks]: this lane's operand
+// chunk of K-step ks (elements 16*ks + 8*(lane/32) .. +7 of its token's row, loaded
+// up front).  tt: T^T of the head in LDS.
+template <typename TIn>
+__device__ __forceinline__ void transform_mfma(const u32x4 (&kop)[8], const uint16_t* tt, int lane,
                                                float (&x)[64]) {
   typedef typename Mfma<TIn>::vec vec;
   const int rho = lane & 31, kk = lane >> 5;
@@ -101,8 +116,7 @@ __device__ __forceinline__ void transform_mfma(const TIn* tok_row, const uint16_
   for (int mt = 0; mt < 4; ++mt) acc[mt] = f32x16{};
 #pragma unroll
   for (int ks = 0; ks < 8; ++ks) {
-    u32x4 braw = *reinterpret_cast<const u32x4*>(tok_row + 16 * ks + 8 * kk);
-    vec b = __builtin_bit_cast(vec, braw);
+    vec b = __builtin_bit_cast(vec, kop[ks]);
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) {
       const int ch = 64 * ((rho >> 2) & 1) + 16 * mt + 4 * (rho >> 3) + (rho & 3);
@@ -306,16 +320,35 @@ __global__ __launch_bounds__(256) void append_kernel(AppendParams p) {
   const TIn* vrow = reinterpret_cast<const TIn*>(p.v) + (i_ld * p.heads + h) * kHeadDim;
   constexpr bool kMfmaType = sizeof(TIn) == 2;
 
+  // 16-bit inputs: every global load this wave needs goes out first (the token's key
+  // operand chunks and value half-row, then this thread's share of T), so the kernel pays
+  // about one memory latency before the arithmetic instead of one per step.
+  u32x4 kraw[8], vraw[8];
   if constexpr (kMfmaType) {
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      // with a transform: the matrix-core operand of K-step q; without: the half-row
+      const int koff = p.t != nullptr ? 16 * q + 8 * hh : 64 * hh + 8 * q;
+      kraw[q] = *reinterpret_cast<const u32x4*>(krow + koff);
+      vraw[q] = *reinterpret_cast<const u32x4*>(vrow + 64 * hh + 8 * q);
+    }
     if (p.t != nullptr) {
       const TIn* th = reinterpret_cast<const TIn*>(p.t) + (int64_t)h * kHeadDim * kHeadDim;
-      for (int idx = threadIdx.x; idx < kHeadDim * 16; idx += 256) {
+      constexpr int kIters = kHeadDim * 16 / 256;
+      u32x4 tw[kIters];
+#pragma unroll
+      for (int it = 0; it < kIters; ++it) {
+        const int idx = (int)threadIdx.x + 256 * it;
+        tw[it] = *reinterpret_cast<const u32x4*>(th + (idx >> 4) * kHeadDim + (idx & 15) * 8);
+      }
+#pragma unroll
+      for (int it = 0; it < kIters; ++it) {
+        const int idx = (int)threadIdx.x + 256 * it;
         const int c = idx >> 4, j0 = (idx & 15) * 8;
-        u32x4 w = *reinterpret_cast<const u32x4*>(th + c * kHeadDim + j0);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          tt[(j0 + 2 * e) * kTtStride + c] = (uint16_t)(w[e] & 0xFFFFu);
-          tt[(j0 + 2 * e + 1) * kTtStride + c] = (uint16_t)(w[e] >> 16);
+          tt[(j0 + 2 * e) * kTtStride + c] = (uint16_t)(tw[it][e] & 0xFFFFu);
+          tt[(j0 + 2 * e + 1) * kTtStride + c] = (uint16_t)(tw[it][e] >> 16);
         }
       }
       __syncthreads();
@@ -326,10 +359,11 @@ __global__ __launch_bounds__(256) void append_kernel(AppendParams p) {
   float lo, hi;
 
   // ---------------- keys ----------------
-  if (p.t == nullptr) {
+  if constexpr (kMfmaType) {
+    if (p.t == nullptr) unpack_half_row<TIn>(kraw, x);
+    else transform_mfma<TIn>(kraw, tt, lane, x);
+  } else if (p.t == nullptr) {
     load_half_row<TIn>(krow + 64 * hh, x);
-  } else if constexpr (kMfmaType) {
-    transform_mfma<TIn>(krow, tt, lane, x);
   } else {
     transform_f32(reinterpret_cast<const float*>(krow),
                   reinterpret_cast<const float*>(p.t) + (int64_t)h * kHeadDim * kHeadDim, hh, x);
@@ -369,7 +403,8 @@ __global__ __launch_bounds__(256) void append_kernel(AppendParams p) {
   }
 
   // ---------------- values ----------------
-  load_half_row<TIn>(vrow + 64 * hh, x);
+  if constexpr (kMfmaType) unpack_half_row<TIn>(vraw, x);
+  else load_half_row<TIn>(vrow + 64 * hh, x);
   clip_bounds<KSEL>(x, p.quant_v, p.alpha_v, p.ilo, p.ihi, p.flo, p.fhi, lane, sortbuf[wave], lo, hi);
   const GroupQuant g = make_quant(lo, hi, p.bits_v);
   const int bits = p.bits_v;
@@ -381,21 +416,22 @@ __global__ __launch_bounds__(256) void append_kernel(AppendParams p) {
   }
   const int64_t slot0 = __shfl(slot, 0);
   const bool aligned_run = __all(valid && slot == slot0 + tl) && (slot0 % kTileTokens) == 0;
-  if (aligned_run) {
-    // codes as bytes [token][channel] in LDS, then whole words of 32/bits tokens
-    uint32_t* vb = vbuf[wave];
+  // codes as bytes [token][channel] in LDS: both write paths read them from there
+  uint32_t* vb = vbuf[wave];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      u32x4 w;
+  for (int q = 0; q < 4; ++q) {
+    u32x4 w;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int m = 16 * q + 4 * e;
-        w[e] = code_of(x[m], g) | (code_of(x[m + 1], g) << 8) | (code_of(x[m + 2], g) << 16) |
-               (code_of(x[m + 3], g) << 24);
-      }
-      *reinterpret_cast<u32x4*>(vb + tl * 32 + 16 * hh + 4 * q) = w;
+    for (int e = 0; e < 4; ++e) {
+      const int m = 16 * q + 4 * e;
+      w[e] = code_of(x[m], g) | (code_of(x[m + 1], g) << 8) | (code_of(x[m + 2], g) << 16) |
+             (code_of(x[m + 3], g) << 24);
     }
-    wave_sync();
+    *reinterpret_cast<u32x4*>(vb + tl * 32 + 16 * hh + 4 * q) = w;
+  }
+  wave_sync();
+  if (aligned_run) {
+    // whole words of 32/bits tokens
     const int o0 = (int)(slot0 % kPageTokens);
     const int cq = lane & 31, part = lane >> 5;
     uint32_t* words = reinterpret_cast<uint32_t*>(p.vpool + ((slot0 / kPageTokens) * p.heads + h) * vbb);
@@ -410,16 +446,26 @@ __global__ __launch_bounds__(256) void append_kernel(AppendParams p) {
       }
       *reinterpret_cast<u32x4*>(words + (o0 / per_word + rw) * kHeadDim + 4 * cq) = w;
     }
-  } else if (valid) {
-    uint32_t* words = reinterpret_cast<uint32_t*>(blk);
+  } else {
+    // token by token, the whole wave merges one token's codes into its 128 words (lane l:
+    // channels l and l + 64), so each atomic instruction covers contiguous words; the
+    // AND/OR merge keeps other tokens' bits of the shared words
     const int per_word = 32 / bits;
-    const int row = o / per_word, sh = (o % per_word) * bits;
-    const uint32_t mask = ((1u << bits) - 1u) << sh;
+    const uint32_t fmask = (1u << bits) - 1u;
+    for (int t = 0; t < kTileTokens; ++t) {
+      const int64_t st = __shfl(slot, t);
+      if (st < 0 || st >= p.num_pages * kPageTokens) continue;   // same for the whole wave
+      const int ot = (int)(st % kPageTokens);
+      const int sh = (ot % per_word) * bits;
+      uint32_t* words = reinterpret_cast<uint32_t*>(p.vpool + ((st / kPageTokens) * p.heads + h) * vbb) +
+                        (ot / per_word) * kHeadDim;
 #pragma unroll
-    for (int m = 0; m < 64; ++m) {
-      uint32_t* w = words + row * kHeadDim + 64 * hh + m;
-      atomicAnd(w, ~mask);
-      atomicOr(w, code_of(x[m], g) << sh);
+      for (int half = 0; half < 2; ++half) {
+        const int c = lane + 64 * half;
+        const uint32_t code = (vb[t * 32 + c / 4] >> (8 * (c % 4))) & fmask;
+        atomicAnd(words + c, ~(fmask << sh));
+        atomicOr(words + c, code << sh);
+      }
     }
   }
 }
