@@ -44,6 +44,7 @@ namespace {
 constexpr int kWaves = 4;
 
 typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ half8 as_half8(u32x4 w) { return __builtin_bit_cast(half8, w); }
 
@@ -63,8 +64,6 @@ __device__ __forceinline__ uint32_t code_pair(uint32_t w, uint32_t w_shifted, in
 }
 template <int B> __device__ __forceinline__ uint32_t shifted(uint32_t w) { return B == 2 ? (w >> 10) : (w >> 8); }
 
-__device__ __forceinline__ float lo_f16(uint32_t w) { return (float)__builtin_bit_cast(half2_t, w)[0]; }
-__device__ __forceinline__ float hi_f16(uint32_t w) { return (float)__builtin_bit_cast(half2_t, w)[1]; }
 
 __device__ __forceinline__ uint32_t pack_f16x2(float a, float b) {
   half2_t h = {(_Float16)a, (_Float16)b};
@@ -401,19 +400,23 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeParams p) {
                                                               sacc[t4 / NB], 0, 0, 0);
       }
     }
-    // metadata of the lane's tokens (4 consecutive per tile: 8 bytes each)
-    float x[A][4], sv[A][4], zv[A][4];
+    // metadata of the lane's tokens (4 consecutive per tile: 8 bytes each).  The fp16
+    // scales and zeros enter the arithmetic as fp16 operands of mixed fma (no conversions).
+    float x[A][4];
+    u32x2 svp[A], zvp[A];
 #pragma unroll
     for (int a = 0; a < A; ++a) {
-      const u32x2 skw = pr.meta[a][0], zkw = pr.meta[a][1], svw = pr.meta[a][2], zvw = pr.meta[a][3];
+      // (the 8-byte pair is reinterpreted whole: building half pairs from its two words
+      // separately is miscompiled by this toolchain, which then reads only the first word)
+      const half4_t sk = __builtin_bit_cast(half4_t, pr.meta[a][0]);
+      const half4_t zk = __builtin_bit_cast(half4_t, pr.meta[a][1]);
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const float sk = (r & 1) ? hi_f16(skw[r >> 1]) : lo_f16(skw[r >> 1]);
-        const float zk = (r & 1) ? hi_f16(zkw[r >> 1]) : lo_f16(zkw[r >> 1]);
-        sv[a][r] = (r & 1) ? hi_f16(svw[r >> 1]) : lo_f16(svw[r >> 1]);
-        zv[a][r] = (r & 1) ? hi_f16(zvw[r >> 1]) : lo_f16(zvw[r >> 1]);
-        x[a][r] = __builtin_fmaf(sacc[a][r], sk, zk * qsf);
+        const float zq = __builtin_fmaf((float)zk[r], qsf, 0.0f);
+        x[a][r] = __builtin_fmaf(sacc[a][r], (float)sk[r], zq);
       }
+      svp[a] = pr.meta[a][2];
+      zvp[a] = pr.meta[a][3];
     }
     if (partial) {                          // absent tokens: no weight, no garbage scale
 #pragma unroll
@@ -422,27 +425,40 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeParams p) {
         for (int r = 0; r < 4; ++r) {
           const bool ok = 16 * kg + 4 * (a * NB + beta) + r < valid_tokens;
           x[a][r] = ok ? x[a][r] : -__builtin_inff();
-          sv[a][r] = ok ? sv[a][r] : 0.0f;
-          zv[a][r] = ok ? zv[a][r] : 0.0f;
+          const uint32_t keep = ok ? 0xFFFFFFFFu : ((r & 1) ? 0x0000FFFFu : 0xFFFF0000u);
+          svp[a][r >> 1] &= keep;
+          zvp[a][r >> 1] &= keep;
         }
     }
     // ---- online softmax, per column ----
     float mx = x[0][0];
-    float svm = sv[0][0];
+    uint32_t svm = 0;                      // largest value-scale bit pattern (s_v >= 0)
 #pragma unroll
-    for (int a = 0; a < A; ++a)
+    for (int a = 0; a < A; ++a) {
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        mx = fmaxf(mx, x[a][r]);
-        svm = fmaxf(svm, sv[a][r]);
-      }
+      for (int r = 0; r < 4; ++r) mx = fmaxf(mx, x[a][r]);
+#pragma unroll
+      for (int e = 0; e < 2; ++e) svm = max(svm, max(svp[a][e] & 0xFFFFu, svp[a][e] >> 16));
+    }
     mx = col_max(mx);
-    // the largest value scale of the column's tokens sets S: P~ < 2^15 keeps fp16 finite
-    const int svbits = col_max_i((int)__builtin_bit_cast(uint32_t, svm));   // sv >= 0
-    const int ev = svbits > 0 ? ((svbits >> 23) & 0xFF) - 127 : -30;
-    const int S_new = min(S, 14 - ev);
-    const float m_new = fmaxf(m, mx);
-    if (__any(m_new > m || S_new != S)) {
+    // Lazy rescaling.  The reference max m of a column moves only when the page's scores
+    // exceed it by more than kLag (log2 units), so p = 2^(F(x - m)) <= 2^kLag; S moves
+    // only when a value scale would push P~ = p s_v 2^(S - vcls) to 2^15 (fp16 range),
+    // and then kSMargin further, so that later pages rarely need it again.  Rescaling is
+    // wave-uniform, so an eager rule would run it whenever any of the 16 columns grows.
+    constexpr float kLag = 8.0f;
+    constexpr int kSMargin = 4;
+    // exponent bound of the column's largest value scale: s_v < 2^(ev+1) (fp16 bits;
+    // a subnormal scale counts as 2^-15)
+    const int svbits = col_max_i((int)svm);
+    const int e16 = (svbits >> 10) & 0x1F;
+    const int ev = svbits == 0 ? -30 : (e16 == 0 ? -15 : e16 - 15);
+    const int S_tight = 14 - (int)kLag - ev;
+    const bool need_s = S_tight < S;
+    const int S_new = need_s ? S_tight - kSMargin : S;
+    const bool need_m = F * (mx - m) > kLag;       // false when the column has no token here
+    const float m_new = need_m ? mx : m;
+    if (__any(need_m || need_s)) {
       const float alpha = exp2f(F * (m - m_new) + (float)(S_new - S));
 #pragma unroll
       for (int mt = 0; mt < 8; ++mt) acc_o[mt] *= alpha;
@@ -463,9 +479,11 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeParams p) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const float pe = __builtin_amdgcn_exp2f(__builtin_fmaf(F, x[a][r], nb[a][r]));
+        const half4_t svh = __builtin_bit_cast(half4_t, svp[a]);
+        const half4_t zvh = __builtin_bit_cast(half4_t, zvp[a]);
         lsum[a][r] += pe;
-        zacc[a][r] = __builtin_fmaf(pe, zv[a][r], zacc[a][r]);
-        pt[a][r] = pe * sv[a][r];
+        zacc[a][r] = __builtin_fmaf(pe, (float)zvh[r], zacc[a][r]);
+        pt[a][r] = __builtin_fmaf(pe, (float)svh[r], 0.0f);
       }
 
     // ---- P.V: B operand element (s, 2*jj + h) is token u = v_token(s, 2jj+h), i.e. tile
