@@ -7,20 +7,23 @@
 // so per-element read work is paid over the whole cache.
 //
 // One kernel (plus a merge when a sequence is split across workgroups): decode_kernel,
-// grid (chunk, KV head, sequence), 4 waves per workgroup.
-//  * Prologue: q' = q T^-T in fp32, scaled to log2 units, turned into the fp16
-//    matrix-core operand each lane holds.  Its loads go out before the first pages' copies
-//    so the arithmetic overlaps them.
-//  * Page walk: each wave walks a run of pages.  Pages are copied HBM -> LDS by the DMA
-//    path (global_load_lds, 16 B a lane, nontemporal) up to NBUF-1 pages ahead of the page
-//    in use, so several pages are in flight per wave without holding registers.
-// Both contractions run on 16x16x32 fp16 matrix cores with fp32 accumulation:
+// grid (chunk, KV head, sequence), 4 waves per workgroup, 2 resident waves per SIMD.
+//  * Prologue: q' = q T^-T in fp32, scaled to log2 units, turned into the matrix-core
+//    operand each lane holds.  Its loads go out before the first pages' loads so the
+//    arithmetic overlaps them.
+//  * Page walk: each wave walks a run of pages through a register ring: the buffer loads
+//    (nontemporal) of page i + PIPE are issued when page i has been used, so PIPE pages
+//    are in flight per wave.
+// Contractions, fp32 accumulation:
 //   scores  S[token][col] = codes_K[token][ch] . q''[ch][col]
 //   output  O[ch][col]   += codes_V[ch][token] . P~[token][col]
-// Codes are never converted arithmetically: an AND of the packed word with a mask
-// leaves, in each 16-bit half, one code at bit b*e of the mantissa of a subnormal fp16,
-// i.e. the exact value code * 2^(b*e) * 2^-24 (codes in the top bits of a half are
-// shifted down first).  The factor 2^-(b*e) is folded into the other operand.
+// 2-bit keys use the scaled fp4 x fp6 16x16x128 product: a 2-bit code in the low bits of
+// an fp4 nibble is the exact value code/2, so one AND yields 8 operands, and q' is carried
+// as three fp6 terms with per-term E8M0 scales (about 12 significant bits, like fp16).
+// 4-bit keys and the P.V product use 16x16x32 fp16 products: an AND of the packed word
+// with a mask leaves, in each 16-bit half, one code at bit b*e of the mantissa of a
+// subnormal fp16, i.e. the exact value code * 2^(b*e) * 2^-24 (codes in the top bits of a
+// half are shifted down first); the factor 2^-(b*e) is folded into the other operand.
 // Scale and zero are applied outside the products:
 //   score_t = s_t * (q . code_t) + z_t * sum(q)
 //   out     = (sum_t p_t s_t code_t + sum_t p_t z_t) / sum_t p_t
@@ -41,7 +44,12 @@
 namespace kvq {
 namespace {
 
-constexpr int kWaves = 4;
+constexpr int kWaves = 4;                 // waves per workgroup
+constexpr int kThreads = 64 * kWaves;
+// Two waves per SIMD: more resident waves measured slower (the SIMD's issue is the limit,
+// not latency), and two leave room for a three-page register ring.
+constexpr int kWavesPerSimd = 2;
+constexpr int kResidentWaves = 256 * 4 * kWavesPerSimd;
 
 typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
@@ -117,6 +125,51 @@ template <int BV> __host__ __device__ constexpr int v_token_class(int u) {
   return BV == 2 ? pair_class<2>(u % 8) : pair_class<4>((u % 8) % 4);
 }
 
+// ---- 2-bit keys on the scaled fp4 x fp6 matrix-core product (16x16x128) ----
+// A 2-bit code c in the low two bits of an fp4 (e2m1) nibble is the exact value c/2, so an
+// AND with 0x33333333 turns a packed word into 8 fp4 operands (its even codes) and a shift
+// plus AND gives the odd ones.  Lane group kg reads words 2kg, 2kg+1 of the token's row
+// (channels 32kg .. 32kg+31); operand element j of the lane is channel k2_channel(kg, j).
+// fp4 and fp6 operands of this product share one layout (lane group g, element j is
+// contraction index 32g + j), and each lane's 32 elements carry their own E8M0 scale.
+__host__ __device__ constexpr int k2_channel(int kg, int j) {
+  return 32 * kg + 16 * (j / 16) + 2 * (j % 8) + (j / 8) % 2;
+}
+constexpr uint32_t kFp4CodeMask = 0x33333333u;
+constexpr int kQTerms = 3;          // fp6 terms of q'': about 12 significant bits together
+
+typedef int v8i __attribute__((ext_vector_type(8)));
+// D = A(fp4, unit scales) . B(fp6 e2m3, scale byte `opsel` of sb) + C; opsel is a constant
+// after unrolling.
+__device__ __forceinline__ f32x4 mma_fp4_fp6(int opsel, const v8i& a, const v8i& b, f32x4 c, int sb) {
+  switch (opsel) {
+    case 0: return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 4, 2, 0, 0x7F7F7F7F, 0, sb);
+    case 1: return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 4, 2, 0, 0x7F7F7F7F, 1, sb);
+    case 2: return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 4, 2, 0, 0x7F7F7F7F, 2, sb);
+    default: return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 4, 2, 0, 0x7F7F7F7F, 3, sb);
+  }
+}
+
+// fp6 e2m3 (1 sign, 2 exponent bits with bias 1, 3 fraction bits; largest 7.5), round to
+// nearest even, for |v| <= 7.5.
+__device__ __forceinline__ uint32_t e2m3_encode(float v) {
+  const float a = fabsf(v);
+  uint32_t mag;
+  if (a < 1.0f) {
+    mag = (uint32_t)rintf(a * 8.0f);                       // 8 encodes 1.0 (exponent 1)
+  } else {
+    const int e = ilogbf(a);                               // 0, 1 or 2
+    mag = (uint32_t)((e + 1) * 8) + (uint32_t)rintf((ldexpf(a, -e) - 1.0f) * 8.0f);
+  }
+  mag = mag > 31u ? 31u : mag;
+  return (v < 0.0f ? 32u : 0u) | mag;
+}
+__device__ __forceinline__ float e2m3_decode(uint32_t c) {
+  const uint32_t mag = c & 31u, e = mag >> 3, m = mag & 7u;
+  const float a = e == 0 ? (float)m * 0.125f : ldexpf(1.0f + (float)m * 0.125f, (int)e - 1);
+  return (c & 32u) ? -a : a;
+}
+
 // ---------------------------------------------------------------------------------
 // decode
 // ---------------------------------------------------------------------------------
@@ -190,7 +243,7 @@ struct IdentityMatrix {
 __device__ constexpr IdentityMatrix kIdentity{};
 
 template <typename TQ, int BK, int BV, int GP>
-__global__ __launch_bounds__(256) void decode_kernel(DecodeParams p) {
+__global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
   constexpr int NB = 16 / GP;        // column blocks
   constexpr int A = GP / 4;          // score accumulators (tiles per column)
   constexpr int PIPE = pipe_depth<BK, BV>();
@@ -241,31 +294,35 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeParams p) {
   // ---- prologue: q' = q T^-T (fp32, log2 units), then the fp16 operand ----
   // Loads of q and T^-T go out first, then the first pages' loads, so the arithmetic below
   // overlaps the page fetch.
-  constexpr int QPER = GP * kHeadDim / 256;  // q elements per thread (GP >= G)
+  constexpr int QPER = (GP * kHeadDim + kThreads - 1) / kThreads;  // q elements per thread
   const TQ* qb = reinterpret_cast<const TQ*>(p.q) + ((int64_t)b * p.heads_q + (int64_t)kvh * G) * kHeadDim;
   float qreg[QPER];
 #pragma unroll
   for (int k = 0; k < QPER; ++k) {   // rows past the group read row 0 and are zeroed below
-    const int idx = (int)threadIdx.x + 256 * k;
+    const int idx = (int)threadIdx.x + kThreads * k;
     qreg[k] = Elem<TQ>::get(qb, idx < G * kHeadDim ? idx : idx % kHeadDim);
   }
-  // lane (quad, cgrp) of wave w: columns j0..j0+3 (j0 = 32w + 4 quad) of rows 16 cgrp..+15
+  // lane (quad, cgrp) of wave w < 4: columns j0..j0+3 (j0 = 32w + 4 quad) of rows
+  // 16 cgrp..+15; the other waves take no part in the product
+  const bool tw = wave < 4;
   const int quad = lane & 7, cgrp = lane >> 3;
-  const int j0 = 32 * wave + 4 * quad;
+  const int j0 = 32 * (tw ? wave : 0) + 4 * quad;
   // both candidates live in global memory; saying so keeps these global (not flat) loads,
   // whose completion the compiler counts precisely
   typedef __attribute__((address_space(1))) const f32x4 gf32x4;
   const gf32x4* tsrc = (const gf32x4*)(p.tinv ? p.tinv + (int64_t)kvh * kHeadDim * kHeadDim : kIdentity.v);
   f32x4 trow[16];
 #pragma unroll
-  for (int cc = 0; cc < 16; ++cc) trow[cc] = tsrc[((16 * cgrp + cc) * kHeadDim + j0) / 4];
+  for (int cc = 0; cc < 16; ++cc) trow[cc] = tw ? tsrc[((16 * cgrp + cc) * kHeadDim + j0) / 4] : f32x4{};
   my_page = (lane < np && my_page >= 0 && my_page < p.num_pages) ? my_page : -1;
   PageRegs<BK, BV, A> ring[PIPE];
 #pragma unroll
   for (int d = 0; d < PIPE; ++d) load(ring[d], d);
 #pragma unroll
-  for (int k = 0; k < QPER; ++k)
-    qs[threadIdx.x + 256 * k] = (int)threadIdx.x + 256 * k < G * kHeadDim ? qreg[k] : 0.0f;
+  for (int k = 0; k < QPER; ++k) {
+    const int idx = (int)threadIdx.x + kThreads * k;
+    if (idx < GP * kHeadDim) qs[idx] = idx < G * kHeadDim ? qreg[k] : 0.0f;
+  }
   lds_barrier();
   float qacc[GP][4];
 #pragma unroll
@@ -290,7 +347,7 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeParams p) {
     }
   }
   lds_barrier();                           // every read of q is done: q' replaces it
-  if (cgrp == 0) {
+  if (tw && cgrp == 0) {
 #pragma unroll
     for (int g = 0; g < GP; ++g)
       if (g < G) {
@@ -303,6 +360,78 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeParams p) {
       }
   }
   lds_barrier();
+  // 2-bit keys: q' as three fp6 terms t_k with scales 2^(e1 - 4k), e1 per head so that
+  // max|q'| 2^-e1 <= 7.5; each term holds the previous remainder to within a quarter of its
+  // scale, so the sum of the three represents q' to about 2^-12 of its largest element.
+  // The product with the fp4 codes (value c/2) gives half of q'.code: F = 2.
+  v8i bq6[kQTerms];
+  int sreg[kQTerms];
+  u32x4 bq[BK == 2 ? 1 : NB][4];     // fp16 operands (4-bit keys)
+  const int gq = n % GP;
+  if constexpr (BK == 2) {
+    uint8_t* qcode = smem;                                         // [term][head][channel]
+    uint32_t* qpack = reinterpret_cast<uint32_t*>(smem + kQTerms * GP * kHeadDim);  // [term][kg][head][6]
+    int* qexp = reinterpret_cast<int*>(qpack + kQTerms * 4 * GP * 6);
+    for (int g = wave; g < GP; g += kWaves) {
+      const float a0 = g < G ? qs[g * kHeadDim + lane] : 0.0f, a1 = g < G ? qs[g * kHeadDim + lane + 64] : 0.0f;
+      float amax = fmaxf(fabsf(a0), fabsf(a1));
+#pragma unroll
+      for (int d = 1; d < 64; d <<= 1) amax = fmaxf(amax, __shfl_xor(amax, d));
+      int e1 = 0;
+      if (amax > 0.0f) {
+        const int E = ilogbf(amax);
+        e1 = ldexpf(amax, 2 - E) <= 7.5f ? E - 2 : E - 1;
+      }
+      e1 = max(e1, -118);                  // the last term's scale stays a normal E8M0 value
+      float r0 = a0, r1 = a1, qsum = 0.0f;
+#pragma unroll
+      for (int k = 0; k < kQTerms; ++k) {
+        const int e = e1 - 4 * k;
+        const uint32_t c0 = e2m3_encode(ldexpf(r0, -e)), c1 = e2m3_encode(ldexpf(r1, -e));
+        const float v0 = ldexpf(e2m3_decode(c0), e), v1 = ldexpf(e2m3_decode(c1), e);
+        r0 -= v0;
+        r1 -= v1;
+        qsum += v0 + v1;
+        qcode[(k * GP + g) * kHeadDim + lane] = (uint8_t)c0;
+        qcode[(k * GP + g) * kHeadDim + lane + 64] = (uint8_t)c1;
+      }
+#pragma unroll
+      for (int d = 1; d < 64; d <<= 1) qsum += __shfl_xor(qsum, d);
+      if (lane == 0) {
+        hconst[2 * g] = qsum;
+        hconst[2 * g + 1] = 2.0f;
+        qexp[g] = e1;
+      }
+    }
+    lds_barrier();
+    // operand words: element j of lane group kg at bits 6j .. 6j+5 of six dwords
+    for (int it = threadIdx.x; it < kQTerms * 4 * GP * 6; it += kThreads) {
+      const int d = it % 6, g = (it / 6) % GP, kgi = (it / (6 * GP)) % 4, k = it / (24 * GP);
+      const uint8_t* src = qcode + (k * GP + g) * kHeadDim;
+      uint32_t word = 0;
+      const int j0 = (32 * d) / 6, j1 = min(31, (32 * d + 31) / 6);
+      for (int j = j0; j <= j1; ++j) {
+        const uint32_t c = src[k2_channel(kgi, j)];
+        const int sh = 6 * j - 32 * d;
+        word |= sh >= 0 ? c << sh : c >> (-sh);
+      }
+      qpack[it] = word;
+    }
+    lds_barrier();
+#pragma unroll
+    for (int k = 0; k < kQTerms; ++k) {
+#pragma unroll
+      for (int d = 0; d < 6; ++d) bq6[k][d] = (int)qpack[((k * 4 + kg) * GP + gq) * 6 + d];
+      bq6[k][6] = 0;
+      bq6[k][7] = 0;
+      // scale byte t (selected per tile by op_sel): the term's scale for this lane's column
+      // block, 2^-127 (contributes nothing) for the others
+      uint32_t s = 0;
+#pragma unroll
+      for (int t = 0; t < NB; ++t) s |= (beta == t ? (uint32_t)(127 + qexp[gq] - 4 * k) : 0u) << (8 * t);
+      sreg[k] = (int)s;
+    }
+  } else {
   // fp16 operand q''[c] = q'[c] * 2^(E - BK*e(c)), E per head so that max|q''| < 2^15
   for (int g = wave; g < G; g += kWaves) {
     const float a0 = qs[g * kHeadDim + lane], a1 = qs[g * kHeadDim + lane + 64];
@@ -329,8 +458,6 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeParams p) {
   lds_barrier();
   // B operand of K-step s for this lane (column n = head n % GP, lane group kg), masked per
   // column block: block beta's operand is the lane's own, the others are zero
-  u32x4 bq[NB][4];
-  const int gq = n % GP;
 #pragma unroll
   for (int s = 0; s < 4; ++s) {
     u32x4 w;
@@ -342,6 +469,7 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeParams p) {
     }
 #pragma unroll
     for (int bb = 0; bb < NB; ++bb) bq[bb][s] = (beta == bb) ? w : u32x4{0u, 0u, 0u, 0u};
+  }
   }
   const float F = gq < G ? hconst[2 * gq + 1] : 1.0f;                  // score = F * x'
   const float qsf = gq < G ? hconst[2 * gq] / hconst[2 * gq + 1] : 0.0f;
@@ -384,6 +512,18 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeParams p) {
     f32x4 sacc[A];
 #pragma unroll
     for (int a = 0; a < A; ++a) sacc[a] = f32x4{};
+    if constexpr (BK == 2) {
+      // one 16x16x128 product per tile and fp6 term; the op_sel'd scale byte keeps tile t4
+      // out of every column block but t4 % NB
+#pragma unroll
+      for (int t4 = 0; t4 < 4; ++t4) {
+        const uint32_t w0 = pr.k[t4][0], w1 = pr.k[t4][1];
+        const v8i av = {(int)(w0 & kFp4CodeMask), (int)((w0 >> 2) & kFp4CodeMask), (int)(w1 & kFp4CodeMask),
+                        (int)((w1 >> 2) & kFp4CodeMask), 0, 0, 0, 0};
+#pragma unroll
+        for (int k = 0; k < kQTerms; ++k) sacc[t4 / NB] = mma_fp4_fp6(t4 % NB, av, bq6[k], sacc[t4 / NB], sreg[k]);
+      }
+    } else
 #pragma unroll
     for (int t4 = 0; t4 < 4; ++t4) {
       uint32_t kw[BK == 2 ? 2 : 4];
@@ -567,7 +707,7 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeParams p) {
 
   // ---- merge the waves and the column blocks of each head ----
   const int hq0 = kvh * G;
-  for (int idx = threadIdx.x; idx < G * kHeadDim; idx += 256) {
+  for (int idx = threadIdx.x; idx < G * kHeadDim; idx += kThreads) {
     const int gg = idx / kHeadDim, ch = idx % kHeadDim;
     float M = -__builtin_inff();
 #pragma unroll
@@ -627,9 +767,9 @@ template <typename TQ, int BK, int BV>
 hipError_t launch_typed(const DecodeParams& p, hipStream_t stream) {
   const dim3 grid((unsigned)p.chunks, (unsigned)p.heads_kv, (unsigned)p.batch);
   switch (p.gpad) {
-    case 4: hipLaunchKernelGGL((decode_kernel<TQ, BK, BV, 4>), grid, dim3(256), 0, stream, p); break;
-    case 8: hipLaunchKernelGGL((decode_kernel<TQ, BK, BV, 8>), grid, dim3(256), 0, stream, p); break;
-    default: hipLaunchKernelGGL((decode_kernel<TQ, BK, BV, 16>), grid, dim3(256), 0, stream, p); break;
+    case 4: hipLaunchKernelGGL((decode_kernel<TQ, BK, BV, 4>), grid, dim3(kThreads), 0, stream, p); break;
+    case 8: hipLaunchKernelGGL((decode_kernel<TQ, BK, BV, 8>), grid, dim3(kThreads), 0, stream, p); break;
+    default: hipLaunchKernelGGL((decode_kernel<TQ, BK, BV, 16>), grid, dim3(kThreads), 0, stream, p); break;
   }
   hipError_t err = hipGetLastError();
   if (err != hipSuccess || p.chunks == 1) return err;
@@ -653,9 +793,9 @@ int decode_group_pad(int group) { return group <= 4 ? 4 : (group <= 8 ? 8 : 16);
 DecodeSplit decode_split(int batch, int heads_kv, int max_seq_len) {
   const int pages = (max_seq_len + kPageTokens - 1) / kPageTokens;
   const int64_t units = (int64_t)batch * heads_kv;
-  // about 2048 waves (one resident round of 8 waves per CU), 4 to 64 pages per wave (a
-  // wave's page ids fit one register, one per lane)
-  int64_t ppw = (units * pages + 2047) / 2048;
+  // about kResidentWaves waves (one resident round), 4 to 64 pages per wave
+  // (a wave's page ids fit one register, one per lane)
+  int64_t ppw = (units * pages + kResidentWaves - 1) / kResidentWaves;
   if (ppw < 4) ppw = 4;
   if (ppw > 64) ppw = 64;
   const int64_t waves = pages > 0 ? (pages + ppw - 1) / ppw : 1;
