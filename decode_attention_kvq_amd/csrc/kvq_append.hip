@@ -334,21 +334,26 @@ __global__ __launch_bounds__(256) void append_kernel(AppendParams p) {
     }
     if (p.t != nullptr) {
       const TIn* th = reinterpret_cast<const TIn*>(p.t) + (int64_t)h * kHeadDim * kHeadDim;
-      constexpr int kIters = kHeadDim * 16 / 256;
-      u32x4 tw[kIters];
+      // T^T into LDS without bank conflicts: wave w, unit u covers rows j0 = 8 (w + 4u) ..
+      // j0 + 7 of T^T; lane l reads T[2l][j0..j0+7] and T[2l+1][j0..j0+7] and writes, per
+      // row, the dword holding columns 2l and 2l+1, so each store is one contiguous row
+      // segment of the wave.
+      u32x4 ta[4], tb[4];
 #pragma unroll
-      for (int it = 0; it < kIters; ++it) {
-        const int idx = (int)threadIdx.x + 256 * it;
-        tw[it] = *reinterpret_cast<const u32x4*>(th + (idx >> 4) * kHeadDim + (idx & 15) * 8);
+      for (int u = 0; u < 4; ++u) {
+        const int j0 = 8 * (wave + 4 * u);
+        ta[u] = *reinterpret_cast<const u32x4*>(th + (2 * lane) * kHeadDim + j0);
+        tb[u] = *reinterpret_cast<const u32x4*>(th + (2 * lane + 1) * kHeadDim + j0);
       }
 #pragma unroll
-      for (int it = 0; it < kIters; ++it) {
-        const int idx = (int)threadIdx.x + 256 * it;
-        const int c = idx >> 4, j0 = (idx & 15) * 8;
+      for (int u = 0; u < 4; ++u) {
+        const int j0 = 8 * (wave + 4 * u);
+        uint32_t* row = reinterpret_cast<uint32_t*>(tt + j0 * kTtStride) + lane;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          tt[(j0 + 2 * e) * kTtStride + c] = (uint16_t)(tw[it][e] & 0xFFFFu);
-          tt[(j0 + 2 * e + 1) * kTtStride + c] = (uint16_t)(tw[it][e] >> 16);
+          // halves: row j0+2e takes the low halves of T[2l] and T[2l+1], row j0+2e+1 the high
+          row[(2 * e) * (kTtStride / 2)] = __builtin_amdgcn_perm(tb[u][e], ta[u][e], 0x05040100u);
+          row[(2 * e + 1) * (kTtStride / 2)] = __builtin_amdgcn_perm(tb[u][e], ta[u][e], 0x07060302u);
         }
       }
       __syncthreads();
