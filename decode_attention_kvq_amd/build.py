@@ -26,8 +26,10 @@ COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
 
 # The read path has no NaN semantics to honour (absent tokens are masked by selects), so
 # max/min need no canonicalisation; the write path keeps strict IEEE behaviour.
-# Matrix-core accumulators stay in ordinary VGPRs (no copies through AGPRs in the loop).
-EXTRA = {"kvq_decode.hip": ["-fno-honor-nans", "-mllvm", "-amdgpu-mfma-vgpr-form"]}
+# Matrix-core accumulators stay in ordinary VGPRs (no copies through AGPRs; the write
+# path's transform results are then its working registers).
+EXTRA = {"kvq_decode.hip": ["-fno-honor-nans", "-mllvm", "-amdgpu-mfma-vgpr-form"],
+         "kvq_append.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def _compile(src: str) -> str:

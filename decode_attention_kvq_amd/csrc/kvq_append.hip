@@ -8,13 +8,15 @@
 // Queries Look" (NOVA-KV project page), "Three requirements": every token takes the
 // same number of bits in a paged cache.
 //
-// Work decomposition (gfx950, wave64).  A workgroup of 4 waves handles 128 consecutive
-// tokens of one KV head; each wave handles 32 tokens.  Lane l owns token l%32 and the
-// channel half hh = l/32 (channels 64*hh .. 64*hh+63), so a token's group lives in
-// two lanes and everything except one cross-lane exchange per group stays in-lane:
-//   * transform: D[out-channel][token] = T^T[out][in] . K^T[in][token] on the matrix
-//     cores (32x32x16, bf16 or f16, fp32 accumulate); the rows of T^T are permuted so
-//     that accumulator register r of M-tile mt on lane half hh is channel
+// Work decomposition (gfx950, wave64).  Grid (token blocks, KV heads, 2): the third index
+// selects keys or values, so the two halves run in separate workgroups.  A workgroup of 4
+// waves handles 128 consecutive tokens of one KV head; each wave handles 32 tokens.  Lane
+// l owns token l%32 and the channel half hh = l/32 (channels 64*hh .. 64*hh+63), so a
+// token's group lives in two lanes and everything except one cross-lane exchange per
+// group stays in-lane:
+//   * transform (keys): D[out-channel][token] = T^T[out][in] . K^T[in][token] on the
+//     matrix cores (32x32x16, bf16 or f16, fp32 accumulate); the rows of T^T are permuted
+//     so that accumulator register r of M-tile mt on lane half hh is channel
 //     64*hh + 16*mt + r.  T^T is staged once per workgroup in LDS.
 //   * percentile clip: bottom-K / top-K insertion networks (v_med3) over the lane's
 //     64 values, one exchange with the partner lane, then the order statistics;
@@ -22,6 +24,7 @@
 //     K smallest/largest use a 128-element bitonic sort across the wavefront.
 //   * rms clip: in-lane pairwise tree over the half, one exchange, correctly rounded
 //     sqrt.
+//   * codes: rint by the fp32 addition of 2^23, packed by shifted integer sums.
 //   * keys: each lane writes its half of the token's row (16 or 32 bytes).
 //   * values: codes are transposed through LDS; when the wave's 32 tokens fill an
 //     aligned run of one page, whole words are stored; otherwise the wave merges one
@@ -232,10 +235,8 @@ __device__ __forceinline__ GroupQuant make_quant(float lo, float hi, int bits) {
   return g;
 }
 
-__device__ __forceinline__ uint32_t code_of(float x, const GroupQuant& g) {
-  const float t = (x - g.zf) * g.r;
-  return (uint32_t)__builtin_amdgcn_fmed3f(rintf(t), 0.0f, g.lmax);
-}
+// (x - zero) * r with two separate roundings (the encoder's definition of the code argument)
+__device__ __forceinline__ float code_arg(float x, const GroupQuant& g) { return (x - g.zf) * g.r; }
 
 #pragma clang fp contract(on)
 
@@ -298,13 +299,45 @@ __device__ __forceinline__ void clip_bounds(const float (&x)[64], int quant, flo
   }
 }
 
+// Codes of a lane's values, packed R = 32/bits to a word (value m at bits bits*(m % R) of
+// word m / R).  rint of t in [0, L] is taken by the fp32 addition of 2^23 (round to nearest
+// even, exact), whose bit pattern is 0x4B000000 + code; the words are summed shifted and the
+// constant sum of the 0x4B000000 terms is removed once per word.
+template <int NW, int BITS>
+__device__ __forceinline__ void pack_codes(const float* x, const GroupQuant& g, uint32_t (&w)[NW]) {
+  constexpr int R = 32 / BITS;
+  constexpr uint32_t kMagic = 0x4B000000u;
+  uint32_t junk = 0;
+#pragma unroll
+  for (int e = 0; e < R; ++e) junk += kMagic << (BITS * e);
+#pragma unroll
+  for (int q = 0; q < NW; ++q) {
+    uint32_t acc = 0u - junk;
+#pragma unroll
+    for (int e = 0; e < R; ++e) {
+      const float t = code_arg(x[R * q + e], g);
+      const float c = __builtin_amdgcn_fmed3f(t, 0.0f, g.lmax) + 8388608.0f;
+      acc += __float_as_uint(c) << (BITS * e);
+    }
+    w[q] = acc;
+  }
+}
+
+// Grid (token blocks, KV heads, 2): blockIdx.z = 0 writes keys, 1 writes values.  A
+// workgroup of 4 waves covers 128 consecutive tokens of one head; lane l of a wave owns
+// token l % 32 and the channel half l / 32.
+// Four resident waves per SIMD (128 VGPRs): measured faster than three despite a few
+// spilled registers, since the waves' loads then overlap other waves' arithmetic.
 template <typename TIn, int KSEL>
-__global__ __launch_bounds__(256) void append_kernel(AppendParams p) {
-  __shared__ __attribute__((aligned(16))) uint16_t tt[kHeadDim * kTtStride];
-  __shared__ __attribute__((aligned(16))) uint32_t vbuf[kWavesPerBlock][kTileTokens * 32];
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void append_kernel(AppendParams p) {
+  // keys: T^T of the head (transform); values: codes as bytes [token][channel] per wave
+  constexpr int kTtBytes = kHeadDim * kTtStride * 2;
+  constexpr int kVbufBytes = kWavesPerBlock * kTileTokens * 32 * 4;
+  __shared__ __attribute__((aligned(16))) uint8_t lds[kTtBytes > kVbufBytes ? kTtBytes : kVbufBytes];
   __shared__ float sortbuf[kWavesPerBlock][kHeadDim];
 
   const int h = blockIdx.y;
+  const bool is_v = blockIdx.z != 0;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int tl = lane & 31, hh = lane >> 5;
   const int64_t tile0 = (int64_t)blockIdx.x * kBlockTokens + wave * kTileTokens;
@@ -315,101 +348,89 @@ __global__ __launch_bounds__(256) void append_kernel(AppendParams p) {
   const bool valid = slot >= 0 && slot < p.num_pages * kPageTokens;   // others are skipped
   const int64_t page = valid ? slot / kPageTokens : 0;
   const int o = valid ? (int)(slot % kPageTokens) : 0;
-
-  const TIn* krow = reinterpret_cast<const TIn*>(p.k) + (i_ld * p.heads + h) * kHeadDim;
-  const TIn* vrow = reinterpret_cast<const TIn*>(p.v) + (i_ld * p.heads + h) * kHeadDim;
+  const TIn* row = reinterpret_cast<const TIn*>(is_v ? p.v : p.k) + (i_ld * p.heads + h) * kHeadDim;
   constexpr bool kMfmaType = sizeof(TIn) == 2;
-
-  // 16-bit inputs: every global load this wave needs goes out first (the token's key
-  // operand chunks and value half-row, then this thread's share of T), so the kernel pays
-  // about one memory latency before the arithmetic instead of one per step.
-  u32x4 kraw[8], vraw[8];
-  if constexpr (kMfmaType) {
-#pragma unroll
-    for (int q = 0; q < 8; ++q) {
-      // with a transform: the matrix-core operand of K-step q; without: the half-row
-      const int koff = p.t != nullptr ? 16 * q + 8 * hh : 64 * hh + 8 * q;
-      kraw[q] = *reinterpret_cast<const u32x4*>(krow + koff);
-      vraw[q] = *reinterpret_cast<const u32x4*>(vrow + 64 * hh + 8 * q);
-    }
-    if (p.t != nullptr) {
-      const TIn* th = reinterpret_cast<const TIn*>(p.t) + (int64_t)h * kHeadDim * kHeadDim;
-      // T^T into LDS without bank conflicts: wave w, unit u covers rows j0 = 8 (w + 4u) ..
-      // j0 + 7 of T^T; lane l reads T[2l][j0..j0+7] and T[2l+1][j0..j0+7] and writes, per
-      // row, the dword holding columns 2l and 2l+1, so each store is one contiguous row
-      // segment of the wave.
-      u32x4 ta[4], tb[4];
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int j0 = 8 * (wave + 4 * u);
-        ta[u] = *reinterpret_cast<const u32x4*>(th + (2 * lane) * kHeadDim + j0);
-        tb[u] = *reinterpret_cast<const u32x4*>(th + (2 * lane + 1) * kHeadDim + j0);
-      }
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int j0 = 8 * (wave + 4 * u);
-        uint32_t* row = reinterpret_cast<uint32_t*>(tt + j0 * kTtStride) + lane;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          // halves: row j0+2e takes the low halves of T[2l] and T[2l+1], row j0+2e+1 the high
-          row[(2 * e) * (kTtStride / 2)] = __builtin_amdgcn_perm(tb[u][e], ta[u][e], 0x05040100u);
-          row[(2 * e + 1) * (kTtStride / 2)] = __builtin_amdgcn_perm(tb[u][e], ta[u][e], 0x07060302u);
-        }
-      }
-      __syncthreads();
-    }
-  }
 
   float x[64];
   float lo, hi;
-
-  // ---------------- keys ----------------
-  if constexpr (kMfmaType) {
-    if (p.t == nullptr) unpack_half_row<TIn>(kraw, x);
-    else transform_mfma<TIn>(kraw, tt, lane, x);
-  } else if (p.t == nullptr) {
-    load_half_row<TIn>(krow + 64 * hh, x);
-  } else {
-    transform_f32(reinterpret_cast<const float*>(krow),
-                  reinterpret_cast<const float*>(p.t) + (int64_t)h * kHeadDim * kHeadDim, hh, x);
-  }
-  clip_bounds<KSEL>(x, p.quant_k, p.alpha_k, p.ilo, p.ihi, p.flo, p.fhi, lane, sortbuf[wave], lo, hi);
-  {
+  if (!is_v) {
+    // ---------------- keys ----------------
+    uint16_t* tt = reinterpret_cast<uint16_t*>(lds);
+    if constexpr (kMfmaType) {
+      // the row loads go out first, then this thread's share of T
+      u32x4 kraw[8];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        // with a transform: the matrix-core operand of K-step q; without: the half-row
+        const int koff = p.t != nullptr ? 16 * q + 8 * hh : 64 * hh + 8 * q;
+        kraw[q] = *reinterpret_cast<const u32x4*>(row + koff);
+      }
+      if (p.t != nullptr) {
+        const TIn* th = reinterpret_cast<const TIn*>(p.t) + (int64_t)h * kHeadDim * kHeadDim;
+        // T^T into LDS without bank conflicts: wave w, unit u covers rows j0 = 8 (w + 4u)
+        // .. j0 + 7 of T^T; lane l reads T[2l][j0..j0+7] and T[2l+1][j0..j0+7] and writes,
+        // per row, the dword holding columns 2l and 2l+1, so each store is one contiguous
+        // row segment of the wave.
+        u32x4 ta[4], tb[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int j0 = 8 * (wave + 4 * u);
+          ta[u] = *reinterpret_cast<const u32x4*>(th + (2 * lane) * kHeadDim + j0);
+          tb[u] = *reinterpret_cast<const u32x4*>(th + (2 * lane + 1) * kHeadDim + j0);
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int j0 = 8 * (wave + 4 * u);
+          uint32_t* trow = reinterpret_cast<uint32_t*>(tt + j0 * kTtStride) + lane;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            // row j0+2e takes the low halves of T[2l] and T[2l+1], row j0+2e+1 the high
+            trow[(2 * e) * (kTtStride / 2)] = __builtin_amdgcn_perm(tb[u][e], ta[u][e], 0x05040100u);
+            trow[(2 * e + 1) * (kTtStride / 2)] = __builtin_amdgcn_perm(tb[u][e], ta[u][e], 0x07060302u);
+          }
+        }
+        __syncthreads();
+        transform_mfma<TIn>(kraw, tt, lane, x);
+      } else {
+        unpack_half_row<TIn>(kraw, x);
+      }
+    } else if (p.t == nullptr) {
+      load_half_row<TIn>(row + 64 * hh, x);
+    } else {
+      transform_f32(reinterpret_cast<const float*>(row),
+                    reinterpret_cast<const float*>(p.t) + (int64_t)h * kHeadDim * kHeadDim, hh, x);
+    }
+    clip_bounds<KSEL>(x, p.quant_k, p.alpha_k, p.ilo, p.ihi, p.flo, p.fhi, lane, sortbuf[wave], lo, hi);
     const GroupQuant g = make_quant(lo, hi, p.bits_k);
     uint8_t* blk = p.kpool + (page * p.heads + h) * (int64_t)block_bytes(p.bits_k);
-    if (valid) {
-      if (p.bits_k == 2) {
-        u32x4 w;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          uint32_t acc = 0;
-#pragma unroll
-          for (int e = 0; e < 16; ++e) acc |= code_of(x[16 * q + e], g) << (2 * e);
-          w[q] = acc;
-        }
-        *reinterpret_cast<u32x4*>(blk + o * 32 + 16 * hh) = w;
-      } else {
-#pragma unroll
-        for (int half = 0; half < 2; ++half) {
-          u32x4 w;
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            uint32_t acc = 0;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) acc |= code_of(x[32 * half + 8 * q + e], g) << (4 * e);
-            w[q] = acc;
-          }
-          *reinterpret_cast<u32x4*>(blk + o * 64 + 32 * hh + 16 * half) = w;
-        }
+    if (p.bits_k == 2) {
+      uint32_t w[4];
+      pack_codes<4, 2>(x, g, w);
+      if (valid) *reinterpret_cast<u32x4*>(blk + o * 32 + 16 * hh) = u32x4{w[0], w[1], w[2], w[3]};
+    } else {
+      uint32_t w[8];
+      pack_codes<8, 4>(x, g, w);
+      if (valid) {
+        *reinterpret_cast<u32x4*>(blk + o * 64 + 32 * hh) = u32x4{w[0], w[1], w[2], w[3]};
+        *reinterpret_cast<u32x4*>(blk + o * 64 + 32 * hh + 16) = u32x4{w[4], w[5], w[6], w[7]};
       }
+    }
+    if (valid) {
       uint16_t* meta = reinterpret_cast<uint16_t*>(blk + code_bytes(p.bits_k));
       meta[hh * kPageTokens + o] = hh ? g.z16 : g.s16;
     }
+    return;
   }
 
   // ---------------- values ----------------
-  if constexpr (kMfmaType) unpack_half_row<TIn>(vraw, x);
-  else load_half_row<TIn>(vrow + 64 * hh, x);
+  if constexpr (kMfmaType) {
+    u32x4 vraw[8];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) vraw[q] = *reinterpret_cast<const u32x4*>(row + 64 * hh + 8 * q);
+    unpack_half_row<TIn>(vraw, x);
+  } else {
+    load_half_row<TIn>(row + 64 * hh, x);
+  }
   clip_bounds<KSEL>(x, p.quant_v, p.alpha_v, p.ilo, p.ihi, p.flo, p.fhi, lane, sortbuf[wave], lo, hi);
   const GroupQuant g = make_quant(lo, hi, p.bits_v);
   const int bits = p.bits_v;
@@ -422,17 +443,13 @@ __global__ __launch_bounds__(256) void append_kernel(AppendParams p) {
   const int64_t slot0 = __shfl(slot, 0);
   const bool aligned_run = __all(valid && slot == slot0 + tl) && (slot0 % kTileTokens) == 0;
   // codes as bytes [token][channel] in LDS: both write paths read them from there
-  uint32_t* vb = vbuf[wave];
+  uint32_t* vb = reinterpret_cast<uint32_t*>(lds) + wave * kTileTokens * 32;
+  {
+    uint32_t w[16];
+    pack_codes<16, 8>(x, g, w);
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    u32x4 w;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int m = 16 * q + 4 * e;
-      w[e] = code_of(x[m], g) | (code_of(x[m + 1], g) << 8) | (code_of(x[m + 2], g) << 16) |
-             (code_of(x[m + 3], g) << 24);
-    }
-    *reinterpret_cast<u32x4*>(vb + tl * 32 + 16 * hh + 4 * q) = w;
+    for (int q = 0; q < 4; ++q)
+      *reinterpret_cast<u32x4*>(vb + tl * 32 + 16 * hh + 4 * q) = u32x4{w[4 * q], w[4 * q + 1], w[4 * q + 2], w[4 * q + 3]};
   }
   wave_sync();
   if (aligned_run) {
@@ -477,7 +494,7 @@ __global__ __launch_bounds__(256) void append_kernel(AppendParams p) {
 
 template <typename TIn>
 hipError_t launch_typed(const AppendParams& p, hipStream_t stream) {
-  dim3 grid((unsigned)((p.n + kBlockTokens - 1) / kBlockTokens), (unsigned)p.heads);
+  dim3 grid((unsigned)((p.n + kBlockTokens - 1) / kBlockTokens), (unsigned)p.heads, 2u);
   dim3 block(256);
   // order statistics needed from the sorted group: ilo, ilo+1, ihi, ihi+1
   auto reach = [](int r) { return r < kHeadDim / 2 ? r + 1 : kHeadDim - r; };
