@@ -323,6 +323,47 @@ __device__ __forceinline__ void pack_codes(const float* x, const GroupQuant& g, 
   }
 }
 
+// Value of lane (lane ^ d) for d = 1, 2, 4, 8 (d < 16: within a row of 16 lanes).
+template <int D> __device__ __forceinline__ uint32_t xor_lane(uint32_t v) {
+  if constexpr (D == 1) return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, false);  // quad [1,0,3,2]
+  if constexpr (D == 2) return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x4E, 0xF, 0xF, false);  // quad [2,3,0,1]
+  if constexpr (D == 4) return (uint32_t)__builtin_amdgcn_ds_swizzle((int)v, (4 << 10) | 0x1F);    // xor 4
+  if constexpr (D == 8) return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x128, 0xF, 0xF, false); // row rotate 8
+  return v;
+}
+
+// Transpose of packed codes across the G = 32/BITS lanes of a group (lanes with equal
+// lane / G): before, lane r's word k holds the codes of its token for G channels (channel
+// j at bits BITS*j); after, lane r's word k holds channel r of those G channels for the G
+// tokens of the group (token t at bits BITS*t).  Butterfly over the lane bits: at step s the
+// lanes r and r ^ 2^s swap the codes whose position differs from their own in bit s, by a
+// rotate and a bit-field merge.
+template <int BITS, int NW>
+__device__ __forceinline__ void transpose_codes(uint32_t (&w)[NW], int lane) {
+  constexpr int STEPS = BITS == 2 ? 4 : 3;
+  constexpr uint32_t kKeep[4] = {BITS == 2 ? 0x33333333u : 0x0F0F0F0Fu, BITS == 2 ? 0x0F0F0F0Fu : 0x00FF00FFu,
+                                 BITS == 2 ? 0x00FF00FFu : 0x0000FFFFu, 0x0000FFFFu};
+#pragma unroll
+  for (int st = 0; st < STEPS; ++st) {
+    const int d = 1 << st;
+    const bool upper = (lane >> st) & 1;
+    const uint32_t keep = upper ? ~kKeep[st] : kKeep[st];
+    const uint32_t amt = upper ? (uint32_t)(BITS * d) : (uint32_t)(32 - BITS * d);
+#pragma unroll
+    for (int k = 0; k < NW; ++k) {
+      uint32_t pv;
+      switch (st) {
+        case 0: pv = xor_lane<1>(w[k]); break;
+        case 1: pv = xor_lane<2>(w[k]); break;
+        case 2: pv = xor_lane<4>(w[k]); break;
+        default: pv = xor_lane<8>(w[k]); break;
+      }
+      const uint32_t rot = __builtin_amdgcn_alignbit(pv, pv, amt);
+      w[k] = (w[k] & keep) | (rot & ~keep);
+    }
+  }
+}
+
 // Grid (token blocks, KV heads, 2): blockIdx.z = 0 writes keys, 1 writes values.  A
 // workgroup of 4 waves covers 128 consecutive tokens of one head; lane l of a wave owns
 // token l % 32 and the channel half l / 32.
@@ -442,7 +483,31 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void a
   }
   const int64_t slot0 = __shfl(slot, 0);
   const bool aligned_run = __all(valid && slot == slot0 + tl) && (slot0 % kTileTokens) == 0;
-  // codes as bytes [token][channel] in LDS: both write paths read them from there
+  if (aligned_run) {
+    // the wave's 32 tokens fill whole words: transpose the packed codes across lanes and
+    // store each word once (lane r of a group of 32/bits lanes: one channel per word)
+    uint32_t* words = reinterpret_cast<uint32_t*>(p.vpool + ((slot0 / kPageTokens) * p.heads + h) * vbb);
+    const int o0 = (int)(slot0 % kPageTokens);
+    if (bits == 2) {
+      uint32_t w[4];
+      pack_codes<4, 2>(x, g, w);
+      transpose_codes<2, 4>(w, lane);
+      const int r = lane & 15, g16 = (lane >> 4) & 1;
+      uint32_t* dst = words + (o0 / 16 + g16) * kHeadDim + 64 * hh + r;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) dst[16 * k] = w[k];
+    } else {
+      uint32_t w[8];
+      pack_codes<8, 4>(x, g, w);
+      transpose_codes<4, 8>(w, lane);
+      const int r = lane & 7, g8 = (lane >> 3) & 3;
+      uint32_t* dst = words + (o0 / 8 + g8) * kHeadDim + 64 * hh + r;
+#pragma unroll
+      for (int k = 0; k < 8; ++k) dst[8 * k] = w[k];
+    }
+    return;
+  }
+  // codes as bytes [token][channel] in LDS for the merge below
   uint32_t* vb = reinterpret_cast<uint32_t*>(lds) + wave * kTileTokens * 32;
   {
     uint32_t w[16];
@@ -452,23 +517,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void a
       *reinterpret_cast<u32x4*>(vb + tl * 32 + 16 * hh + 4 * q) = u32x4{w[4 * q], w[4 * q + 1], w[4 * q + 2], w[4 * q + 3]};
   }
   wave_sync();
-  if (aligned_run) {
-    // whole words of 32/bits tokens
-    const int o0 = (int)(slot0 % kPageTokens);
-    const int cq = lane & 31, part = lane >> 5;
-    uint32_t* words = reinterpret_cast<uint32_t*>(p.vpool + ((slot0 / kPageTokens) * p.heads + h) * vbb);
-    const int per_word = 32 / bits;
-    const int rows = kTileTokens / per_word;        // word rows written by the wave
-    for (int rw = part; rw < rows; rw += 2) {
-      u32x4 w = {0u, 0u, 0u, 0u};
-      for (int t = 0; t < per_word; ++t) {
-        const uint32_t d = vb[(rw * per_word + t) * 32 + cq];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) w[e] |= ((d >> (8 * e)) & 0xFFu) << (bits * t);
-      }
-      *reinterpret_cast<u32x4*>(words + (o0 / per_word + rw) * kHeadDim + 4 * cq) = w;
-    }
-  } else {
+  {
     // token by token, the whole wave merges one token's codes into its 128 words (lane l:
     // channels l and l + 64), so each atomic instruction covers contiguous words; the
     // AND/OR merge keeps other tokens' bits of the shared words
@@ -492,8 +541,147 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void a
   }
 }
 
+// ---------------------------------------------------------------------------------
+// Small batches (a decode step's new tokens): one workgroup of two waves per (token, KV
+// head); wave 0 writes the key, wave 1 the value, so the whole step is a few hundred
+// instructions deep.  Lane l holds channels 2l and 2l+1 of the token.
+// ---------------------------------------------------------------------------------
+constexpr int kSmallMaxTokens = 512;    // at most this many tokens use the small path
+
+template <typename TIn> __device__ __forceinline__ float2 load_pair(const TIn* row, int l) {
+  if constexpr (sizeof(TIn) == 4) {
+    return reinterpret_cast<const float2*>(row)[l];
+  } else {
+    constexpr bool bf = __is_same(TIn, __bf16);
+    const uint32_t w = reinterpret_cast<const uint32_t*>(row)[l];
+    return float2{half_lo_to_f32(w, bf), half_hi_to_f32(w, bf)};
+  }
+}
+
+// Bitonic sort of the wave's 128 values (element i: lane i's a for i < 64, lane i-64's b),
+// ascending.
+__device__ __forceinline__ void wave_sort128(float& a, float& b, int lane) {
+  for (int k = 2; k <= kHeadDim; k <<= 1) {
+    for (int j = k >> 1; j >= 1; j >>= 1) {
+      if (j == 64) {
+        const float mn = fminf(a, b), mx = fmaxf(a, b);
+        a = mn;
+        b = mx;
+      } else {
+        const float pa = __shfl_xor(a, j), pb = __shfl_xor(b, j);
+        const bool up_a = (lane & k) == 0, up_b = ((lane + 64) & k) == 0;
+        const bool low = (lane & j) == 0;
+        a = (low == up_a) ? fminf(a, pa) : fmaxf(a, pa);
+        b = (low == up_b) ? fminf(b, pb) : fmaxf(b, pb);
+      }
+    }
+  }
+}
+// Sorted element r (uniform r).
+__device__ __forceinline__ float sorted_at(float a, float b, int r) {
+  return r < 64 ? __shfl(a, r) : __shfl(b, r - 64);
+}
+
+#pragma clang fp contract(off)
+// Sum of squares in the encoder's order: per 64-channel half a pairwise tree over the
+// channel index (stride 32 .. 1), then the halves added.  Channel 2l+e is (lane l, e).
+__device__ __forceinline__ float wave_rms_bound(float a, float b, int lane, float alpha) {
+  float sa = a * a, sb = b * b;
+  const int m = lane & 31;                      // position of the lane within its half / 2
+  for (int st = 16; st >= 1; st >>= 1) {        // channel strides 32 .. 2
+    const float pa = __shfl(sa, lane + st), pb = __shfl(sb, lane + st);
+    if (m < st) {
+      sa = sa + pa;
+      sb = sb + pb;
+    }
+  }
+  sa = sa + sb;                                 // channel stride 1
+  const float total = __shfl(sa, 0) + __shfl(sa, 32);
+  return alpha * sqrtf(total / 128.0f);
+}
+#pragma clang fp contract(on)
+
+template <typename TIn>
+__global__ __launch_bounds__(128) void append_small_kernel(AppendParams p) {
+  const int64_t i = blockIdx.x;
+  const int h = blockIdx.y;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const bool is_v = wave == 1;
+  const int64_t slot = p.slots[i];
+  if (slot < 0 || slot >= p.num_pages * kPageTokens) return;   // skipped (whole workgroup)
+  const int64_t page = slot / kPageTokens;
+  const int o = (int)(slot % kPageTokens);
+  const TIn* row = reinterpret_cast<const TIn*>(is_v ? p.v : p.k) + (i * p.heads + h) * kHeadDim;
+
+  float a, b;                                   // channels 2 lane, 2 lane + 1
+  if (!is_v && p.t != nullptr) {
+    // k' = k . T, fp32 fused multiply-adds with c ascending
+    const TIn* th = reinterpret_cast<const TIn*>(p.t) + (int64_t)h * kHeadDim * kHeadDim;
+    a = 0.0f;
+    b = 0.0f;
+#pragma unroll 16
+    for (int c = 0; c < kHeadDim; ++c) {
+      const float kc = Elem<TIn>::get(row, c);
+      const float2 t = load_pair<TIn>(th + c * kHeadDim, lane);
+      a = __builtin_fmaf(kc, t.x, a);
+      b = __builtin_fmaf(kc, t.y, b);
+    }
+  } else {
+    const float2 v = load_pair<TIn>(row, lane);
+    a = v.x;
+    b = v.y;
+  }
+
+  const int quant = is_v ? p.quant_v : p.quant_k;
+  const int bits = is_v ? p.bits_v : p.bits_k;
+  float lo, hi;
+  if (quant == 1) {
+    const float cl = wave_rms_bound(a, b, lane, is_v ? p.alpha_v : p.alpha_k);
+    lo = -cl;
+    hi = cl;
+  } else {
+    float sa = a, sb = b;
+    wave_sort128(sa, sb, lane);
+    const int ilo1 = p.ilo + 1 < kHeadDim ? p.ilo + 1 : kHeadDim - 1;
+    const int ihi1 = p.ihi + 1 < kHeadDim ? p.ihi + 1 : kHeadDim - 1;
+    lo = interpolate(sorted_at(sa, sb, p.ilo), sorted_at(sa, sb, ilo1), p.flo);
+    hi = interpolate(sorted_at(sa, sb, p.ihi), sorted_at(sa, sb, ihi1), p.fhi);
+  }
+  const GroupQuant g = make_quant(lo, hi, bits);
+  // rint by the fp32 addition of 2^23 (the sum's bit pattern is 0x4B000000 + code)
+  const uint32_t code_a = __float_as_uint(__builtin_amdgcn_fmed3f(code_arg(a, g), 0.0f, g.lmax) + 8388608.0f) - 0x4B000000u;
+  const uint32_t code_b = __float_as_uint(__builtin_amdgcn_fmed3f(code_arg(b, g), 0.0f, g.lmax) + 8388608.0f) - 0x4B000000u;
+  uint8_t* blk = (is_v ? p.vpool : p.kpool) + (page * p.heads + h) * (int64_t)block_bytes(bits);
+  if (lane < 2) {
+    uint16_t* meta = reinterpret_cast<uint16_t*>(blk + code_bytes(bits));
+    meta[lane * kPageTokens + o] = lane ? g.z16 : g.s16;
+  }
+  if (!is_v) {
+    // token row: word w of 32/bits channels; lane l's pair sits at bits 2*bits*(l % (16/bits))
+    const int lpw = 16 / bits;                  // lanes per word
+    uint32_t wv = (code_a | (code_b << bits)) << (2 * bits * (lane % lpw));
+    for (int d = 1; d < lpw; d <<= 1) wv |= (uint32_t)__shfl_xor((int)wv, d);
+    if (lane % lpw == 0) reinterpret_cast<uint32_t*>(blk + o * (kHeadDim * bits / 8))[lane / lpw] = wv;
+  } else {
+    // channel-major words: channel c's word (o / R) at bits bits * (o % R); other tokens'
+    // bits of the words are kept
+    const int R = 32 / bits;
+    const uint32_t fmask = (1u << bits) - 1u;
+    const int sh = (o % R) * bits;
+    uint32_t* words = reinterpret_cast<uint32_t*>(blk) + (o / R) * kHeadDim + 2 * lane;
+    atomicAnd(words, ~(fmask << sh));
+    atomicOr(words, code_a << sh);
+    atomicAnd(words + 1, ~(fmask << sh));
+    atomicOr(words + 1, code_b << sh);
+  }
+}
+
 template <typename TIn>
 hipError_t launch_typed(const AppendParams& p, hipStream_t stream) {
+  if (p.n <= kSmallMaxTokens) {
+    hipLaunchKernelGGL((append_small_kernel<TIn>), dim3((unsigned)p.n, (unsigned)p.heads), dim3(128), 0, stream, p);
+    return hipGetLastError();
+  }
   dim3 grid((unsigned)((p.n + kBlockTokens - 1) / kBlockTokens), (unsigned)p.heads, 2u);
   dim3 block(256);
   // order statistics needed from the sorted group: ilo, ilo+1, ihi, ihi+1

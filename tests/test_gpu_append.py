@@ -8,6 +8,8 @@ Stage B: bf16/f16 inputs with a dense transform on the matrix cores -> value cod
          accumulation), scale/zero off by at most one fp16 ulp on few groups;
          the identity transform is bit-identical to no transform.
 """
+import zlib
+
 import numpy as np
 import pytest
 import torch
@@ -62,13 +64,16 @@ def _run_both(k, v, slots, num_pages, H, bits, quant, rng, t=None, t_oracle="sam
     return cache.k_pages.cpu().numpy(), cache.v_pages.cpu().numpy(), kp, vp
 
 
+# Batches of up to 512 tokens take the one-token-per-workgroup path, larger ones the
+# 128-token-tile path: each test runs a size on both sides of that boundary.
+@pytest.mark.parametrize("n", [300, 700])
 @pytest.mark.parametrize("bits", [(2, 2), (4, 4), (2, 4)])
 @pytest.mark.parametrize("quant", [("percentile", "percentile"), ("rms", "rms"), ("percentile", "rms")])
 @pytest.mark.parametrize("layout", ["aligned", "scattered"])
-def test_stage_a_bit_exact(bits, quant, layout):
-    rng = np.random.default_rng(hash((bits, quant, layout)) % 2**32)
-    H, n = 2, 300                      # 3 workgroups, ragged last wave
-    num_pages = 8
+def test_stage_a_bit_exact(bits, quant, layout, n):
+    rng = np.random.default_rng(zlib.crc32(repr((bits, quant, layout, n)).encode()))
+    H = 2                              # n = 700: 6 tile workgroups, ragged last wave
+    num_pages = n // 64 + 4
     k, v = _inputs(n, H, rng)
     if layout == "aligned":
         slots = np.arange(n, dtype=np.int64) + 64      # page 1 onwards, 32-token aligned
@@ -80,14 +85,15 @@ def test_stage_a_bit_exact(bits, quant, layout):
     assert np.array_equal(gv, ov), describe_mismatch(gv, ov)
 
 
+@pytest.mark.parametrize("n", [100, 600])
 @pytest.mark.parametrize("p", [(0.05, 0.9), (0.25, 0.75), (0.0, 1.0), (1.0, 1.0)])
-def test_stage_a_other_percentiles(p):
-    """Selection networks of width 8 and the bitonic-sort path."""
+def test_stage_a_other_percentiles(p, n):
+    """Selection networks of width 8 and the bitonic-sort paths."""
     rng = np.random.default_rng(11)
-    H, n = 1, 100
+    H = 1
     k, v = _inputs(n, H, rng)
     slots = np.arange(n, dtype=np.int64)
-    gk, gv, ok, ov = _run_both(k, v, slots, 2, H, (4, 2), ("percentile", "percentile"), rng, p=p)
+    gk, gv, ok, ov = _run_both(k, v, slots, n // 64 + 1, H, (4, 2), ("percentile", "percentile"), rng, p=p)
     assert np.array_equal(gk, ok), describe_mismatch(gk, ok)
     assert np.array_equal(gv, ov), describe_mismatch(gv, ov)
 
@@ -112,11 +118,13 @@ def test_append_one_token_at_a_time_preserves_neighbours():
     assert np.array_equal(cache.v_pages.cpu().numpy(), vp)
 
 
+@pytest.mark.parametrize("n", [512, 1024])
 @pytest.mark.parametrize("dtype", ["bf16", "f16"])
 @pytest.mark.parametrize("bits", [(2, 2), (4, 4)])
-def test_stage_b_transform_on_matrix_cores(dtype, bits):
+def test_stage_b_transform_on_matrix_cores(dtype, bits, n):
+    """n = 512: fp32 transform, one token per workgroup; n = 1024: matrix-core transform."""
     rng = np.random.default_rng(13)
-    H, n, G = 2, 512, 4
+    H, G = 2, 4
     k, v = _inputs(n, H, rng, dtype=dtype, config=1)
     ts = []
     for h in range(H):
@@ -139,14 +147,15 @@ def test_stage_b_transform_on_matrix_cores(dtype, bits):
     assert np.all(f16_ulp_distance(gs, os_) <= 1) and np.all(f16_ulp_distance(gz, oz) <= 1)
 
 
+@pytest.mark.parametrize("n", [200, 600])
 @pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
-def test_identity_transform_is_bit_exact(dtype):
+def test_identity_transform_is_bit_exact(dtype, n):
     rng = np.random.default_rng(14)
-    H, n = 2, 200
+    H = 2
     k, v = _inputs(n, H, rng, dtype=dtype)
     eye = np.broadcast_to(np.eye(128, dtype=np.float32), (H, 128, 128)).copy()
     tdt = {"bf16": torch.bfloat16, "f16": torch.float16, "f32": torch.float32}[dtype]
-    gk, gv, ok, ov = _run_both(k, v, np.arange(n, dtype=np.int64), 4, H, (2, 2),
+    gk, gv, ok, ov = _run_both(k, v, np.arange(n, dtype=np.int64), n // 64 + 1, H, (2, 2),
                                ("percentile", "rms"), rng, t=eye, t_oracle=None, torch_dtype=tdt)
     assert np.array_equal(gk, ok), describe_mismatch(gk, ok)
     assert np.array_equal(gv, ov), describe_mismatch(gv, ov)
