@@ -6,9 +6,9 @@ codes) followed by kvq_decode_attn over every cached token.  Default workload: t
 Qwen3-8B-shaped layer (32 query heads, 8 KV heads, head_dim 128) at batch 64 x 16384
 cached tokens, 2-bit K and V, synthetic Sigma-model data, caches resident in HBM.
 
-Each timed region replays HIP graphs captured from the library calls (the calls launch
-on torch's current stream, which the capture records), so host-side call cost does not
-pace the GPU.  Prints one JSON line.  `value` is cached tokens read per second (batch x
+Each timed region is one replay of a HIP graph of K consecutive steps captured from the
+library calls (the calls launch on torch's current stream, which the capture records), so
+host-side call cost does not pace the GPU.  Prints one JSON line.  `value` is cached tokens read per second (batch x
 context per step time).  `roofline` is for the decode kernel: algorithmic bytes per launch
 over its average launch time (HIP events around replays of a decode-only graph on the
 launch stream) against 8 TB/s.  `cpu_baseline`
@@ -18,7 +18,6 @@ from __future__ import annotations
 
 import argparse
 import json
-import math
 import os
 import sys
 import time
@@ -95,12 +94,11 @@ def setup_decode(w, torch, api, calib, synth, dev):
 
 
 def time_steps(w, s, torch, api, steps, warmup):
-    """Times the step as HIP-graph replays, so the host's per-call cost does not pace the
-    GPU.  A graph holds `inner` = gcd(warmup, steps) consecutive steps; warmup/inner
-    untimed replays then steps/inner timed ones (events on the launch stream, plus host
-    wall clock) give exactly `warmup` untimed and `steps` timed steps.  Graphs holding only
-    the append or only the decode call, timed the same way, give each call's average."""
-    inner = max(1, math.gcd(max(warmup, 1), steps))
+    """Times the step as one HIP-graph replay of `steps` consecutive steps (captured from the
+    library calls, which launch on torch's current stream), after one replay of a graph of
+    `warmup` steps, so the host's per-call and per-replay cost does not pace the GPU.  HIP
+    events on the launch stream bracket the timed replay.  Graphs holding only the append
+    or only the decode calls, timed the same way, give each call's average."""
 
     def append():
         api.kvq_quantize_append(s["cache"], s["knew"], s["vnew"], s["new_slots"], t_k=s["t_k"])
@@ -115,31 +113,33 @@ def time_steps(w, s, torch, api, steps, warmup):
 
     step()                                   # first call (library load) outside the graphs
     torch.cuda.synchronize()
-    graphs = {}
-    for name, fn in (("step", step), ("append", append), ("decode", decode)):
+
+    def capture(fn, count):
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
-            for _ in range(inner):
+            for _ in range(count):
                 fn()
-        graphs[name] = g
-    torch.cuda.synchronize()
+        return g
 
-    def timed(g):
-        for _ in range(max(warmup, 1) // inner):
-            g.replay()
+    def timed(fn):
+        gw, gt = capture(fn, max(warmup, 1)), capture(fn, steps)
+        torch.cuda.synchronize()
+        gw.replay()
         torch.cuda.synchronize()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         t0 = time.perf_counter()
         e0.record()
-        for _ in range(steps // inner):
-            g.replay()
+        gt.replay()
         e1.record()
         torch.cuda.synchronize()
-        return e0.elapsed_time(e1) / steps, (time.perf_counter() - t0) * 1e3 / steps
+        ms = e0.elapsed_time(e1) / steps
+        wall = (time.perf_counter() - t0) * 1e3 / steps
+        del gw, gt
+        return ms, wall
 
-    ms_step, wall_step = timed(graphs["step"])
-    ms_app, _ = timed(graphs["append"])
-    ms_dec, _ = timed(graphs["decode"])
+    ms_step, wall_step = timed(step)
+    ms_app, _ = timed(append)
+    ms_dec, _ = timed(decode)
     return ms_step, wall_step, ms_app, ms_dec
 
 

@@ -542,9 +542,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void a
 }
 
 // ---------------------------------------------------------------------------------
-// Small batches (a decode step's new tokens): one workgroup of two waves per (token, KV
-// head); wave 0 writes the key, wave 1 the value, so the whole step is a few hundred
-// instructions deep.  Lane l holds channels 2l and 2l+1 of the token.
+// Small batches (a decode step's new tokens): one workgroup per (token, KV head), so the
+// whole step is a few hundred instructions deep.  Lane l holds channels 2l and 2l+1.
 // ---------------------------------------------------------------------------------
 constexpr int kSmallMaxTokens = 512;    // at most this many tokens use the small path
 
@@ -582,63 +581,97 @@ __device__ __forceinline__ float sorted_at(float a, float b, int r) {
   return r < 64 ? __shfl(a, r) : __shfl(b, r - 64);
 }
 
+// Cross-lane exchanges on the VALU (no LDS): the two values of a lane pair, in some
+// order, for the pairings lane ^ 1, ^ 2 (quad permutes), 7 - lane within 8 (half-row
+// mirror), lane ^ 8 (row rotate), lane ^ 16 and lane ^ 32 (row swaps).  Every use below is
+// symmetric in the pair.
+template <int LVL>
+__device__ __forceinline__ void pair_of(float v, float& x0, float& x1) {
+  const int u = __float_as_int(v);
+  if constexpr (LVL <= 3) {
+    constexpr int ctrl = LVL == 0 ? 0xB1 : LVL == 1 ? 0x4E : LVL == 2 ? 0x141 : 0x128;
+    x0 = v;
+    x1 = __int_as_float(__builtin_amdgcn_mov_dpp(u, ctrl, 0xF, 0xF, false));
+  } else {
+    auto r = LVL == 4 ? __builtin_amdgcn_permlane16_swap((uint32_t)u, (uint32_t)u, false, false)
+                      : __builtin_amdgcn_permlane32_swap((uint32_t)u, (uint32_t)u, false, false);
+    x0 = __uint_as_float((uint32_t)r[0]);
+    x1 = __uint_as_float((uint32_t)r[1]);
+  }
+}
+
+// Bottom-3 / top-3 of the wave's 128 values (2 a lane), in every lane: each lane starts
+// from its pair, then six levels merge two sorted triples (k-th smallest of two sorted
+// lists: the smallest over splits of max(A[i-1], B[k-1-i])).
+template <int LVL>
+__device__ __forceinline__ void merge3(float (&lo)[3], float (&hi)[3]) {
+  float l0[3], l1[3], h0[3], h1[3];
+#pragma unroll
+  for (int k = 0; k < 3; ++k) {
+    pair_of<LVL>(lo[k], l0[k], l1[k]);
+    pair_of<LVL>(hi[k], h0[k], h1[k]);
+  }
+  lo[0] = fminf(l0[0], l1[0]);
+  lo[1] = fminf(fminf(l0[1], l1[1]), fmaxf(l0[0], l1[0]));
+  lo[2] = fminf(fminf(l0[2], l1[2]), fminf(fmaxf(l0[0], l1[1]), fmaxf(l0[1], l1[0])));
+  hi[0] = fmaxf(h0[0], h1[0]);
+  hi[1] = fmaxf(fmaxf(h0[1], h1[1]), fminf(h0[0], h1[0]));
+  hi[2] = fmaxf(fmaxf(h0[2], h1[2]), fmaxf(fminf(h0[0], h1[1]), fminf(h0[1], h1[0])));
+}
+__device__ __forceinline__ void wave_extremes3(float a, float b, float (&lo)[3], float (&hi)[3]) {
+  lo[0] = fminf(a, b);
+  lo[1] = fmaxf(a, b);
+  lo[2] = __builtin_inff();
+  hi[0] = lo[1];
+  hi[1] = lo[0];
+  hi[2] = -__builtin_inff();
+  merge3<0>(lo, hi);
+  merge3<1>(lo, hi);
+  merge3<2>(lo, hi);
+  merge3<3>(lo, hi);
+  merge3<4>(lo, hi);
+  merge3<5>(lo, hi);
+}
+
 #pragma clang fp contract(off)
 // Sum of squares in the encoder's order: per 64-channel half a pairwise tree over the
-// channel index (stride 32 .. 1), then the halves added.  Channel 2l+e is (lane l, e).
-__device__ __forceinline__ float wave_rms_bound(float a, float b, int lane, float alpha) {
-  float sa = a * a, sb = b * b;
-  const int m = lane & 31;                      // position of the lane within its half / 2
-  for (int st = 16; st >= 1; st >>= 1) {        // channel strides 32 .. 2
-    const float pa = __shfl(sa, lane + st), pb = __shfl(sb, lane + st);
-    if (m < st) {
-      sa = sa + pa;
-      sb = sb + pb;
-    }
-  }
-  sa = sa + sb;                                 // channel stride 1
-  const float total = __shfl(sa, 0) + __shfl(sa, 32);
-  return alpha * sqrtf(total / 128.0f);
+// channel index (stride 32 .. 1), then the halves added.  Channel 2l+e is (lane l, e), so
+// channel strides 32 .. 2 pair lanes m and m + 16 .. m + 1 (lane ^ 16 .. ^ 1 for the lanes
+// m < stride whose sums the tree keeps); additions commute, so each level adds the pair.
+__device__ __forceinline__ float wave_rms_bound(float a, float b, float alpha) {
+  float sa = a * a, sb = b * b, x0, x1, y0, y1;
+  pair_of<4>(sa, x0, x1); pair_of<4>(sb, y0, y1); sa = x0 + x1; sb = y0 + y1;     // 32
+  pair_of<3>(sa, x0, x1); pair_of<3>(sb, y0, y1); sa = x0 + x1; sb = y0 + y1;     // 16
+  x1 = __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(sa), (4 << 10) | 0x1F));
+  y1 = __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(sb), (4 << 10) | 0x1F));
+  sa = sa + x1; sb = sb + y1;                                                     // 8
+  pair_of<1>(sa, x0, x1); pair_of<1>(sb, y0, y1); sa = x0 + x1; sb = y0 + y1;     // 4
+  pair_of<0>(sa, x0, x1); pair_of<0>(sb, y0, y1); sa = x0 + x1; sb = y0 + y1;     // 2
+  sa = sa + sb;                                                                   // 1
+  pair_of<5>(sa, x0, x1);                                                         // halves
+  return alpha * sqrtf((x0 + x1) / 128.0f);
 }
 #pragma clang fp contract(on)
 
-template <typename TIn>
-__global__ __launch_bounds__(128) void append_small_kernel(AppendParams p) {
-  const int64_t i = blockIdx.x;
-  const int h = blockIdx.y;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const bool is_v = wave == 1;
-  const int64_t slot = p.slots[i];
-  if (slot < 0 || slot >= p.num_pages * kPageTokens) return;   // skipped (whole workgroup)
-  const int64_t page = slot / kPageTokens;
-  const int o = (int)(slot % kPageTokens);
-  const TIn* row = reinterpret_cast<const TIn*>(is_v ? p.v : p.k) + (i * p.heads + h) * kHeadDim;
-
-  float a, b;                                   // channels 2 lane, 2 lane + 1
-  if (!is_v && p.t != nullptr) {
-    // k' = k . T, fp32 fused multiply-adds with c ascending
-    const TIn* th = reinterpret_cast<const TIn*>(p.t) + (int64_t)h * kHeadDim * kHeadDim;
-    a = 0.0f;
-    b = 0.0f;
-#pragma unroll 16
-    for (int c = 0; c < kHeadDim; ++c) {
-      const float kc = Elem<TIn>::get(row, c);
-      const float2 t = load_pair<TIn>(th + c * kHeadDim, lane);
-      a = __builtin_fmaf(kc, t.x, a);
-      b = __builtin_fmaf(kc, t.y, b);
-    }
-  } else {
-    const float2 v = load_pair<TIn>(row, lane);
-    a = v.x;
-    b = v.y;
-  }
-
+// Quantizes the token's 128 values (lane l: channels 2l, 2l+1) and stores codes and
+// metadata of one (token, head) in the key (is_v = false) or value block.
+template <int KSEL>
+__device__ __forceinline__ void small_quantize_store(float a, float b, bool is_v, int64_t page, int o, int h,
+                                                     int lane, const AppendParams& p) {
   const int quant = is_v ? p.quant_v : p.quant_k;
   const int bits = is_v ? p.bits_v : p.bits_k;
   float lo, hi;
   if (quant == 1) {
-    const float cl = wave_rms_bound(a, b, lane, is_v ? p.alpha_v : p.alpha_k);
+    const float cl = wave_rms_bound(a, b, is_v ? p.alpha_v : p.alpha_k);
     lo = -cl;
     hi = cl;
+  } else if (KSEL == 3) {
+    float bl[3], bh[3];
+    wave_extremes3(a, b, bl, bh);
+    const int ilo1 = p.ilo + 1 < kHeadDim ? p.ilo + 1 : kHeadDim - 1;
+    const int ihi1 = p.ihi + 1 < kHeadDim ? p.ihi + 1 : kHeadDim - 1;
+    lo = interpolate(order_stat<3>(bl, bh, p.ilo), order_stat<3>(bl, bh, ilo1), p.flo);
+    hi = interpolate(order_stat<3>(bl, bh, p.ihi), order_stat<3>(bl, bh, ihi1), p.fhi);
   } else {
     float sa = a, sb = b;
     wave_sort128(sa, sb, lane);
@@ -660,7 +693,10 @@ __global__ __launch_bounds__(128) void append_small_kernel(AppendParams p) {
     // token row: word w of 32/bits channels; lane l's pair sits at bits 2*bits*(l % (16/bits))
     const int lpw = 16 / bits;                  // lanes per word
     uint32_t wv = (code_a | (code_b << bits)) << (2 * bits * (lane % lpw));
-    for (int d = 1; d < lpw; d <<= 1) wv |= (uint32_t)__shfl_xor((int)wv, d);
+    // OR over the word's lanes: quad permutes, then (8 lanes) the half-row mirror
+    wv |= (uint32_t)__builtin_amdgcn_mov_dpp((int)wv, 0xB1, 0xF, 0xF, false);
+    wv |= (uint32_t)__builtin_amdgcn_mov_dpp((int)wv, 0x4E, 0xF, 0xF, false);
+    if (lpw == 8) wv |= (uint32_t)__builtin_amdgcn_mov_dpp((int)wv, 0x141, 0xF, 0xF, false);
     if (lane % lpw == 0) reinterpret_cast<uint32_t*>(blk + o * (kHeadDim * bits / 8))[lane / lpw] = wv;
   } else {
     // channel-major words: channel c's word (o / R) at bits bits * (o % R); other tokens'
@@ -676,14 +712,57 @@ __global__ __launch_bounds__(128) void append_small_kernel(AppendParams p) {
   }
 }
 
+// Five waves per (token, KV head): waves 0-3 each multiply a quarter of the rows of T (all
+// their loads in flight at once), wave 0 then adds the four partial products in order and
+// writes the key; wave 4 writes the value.
+constexpr int kSmallWaves = 5;
+template <typename TIn, int KSEL>
+__global__ __launch_bounds__(64 * kSmallWaves) void append_small_kernel(AppendParams p) {
+  __shared__ float part[4][kHeadDim];
+  const int64_t i = blockIdx.x;
+  const int h = blockIdx.y;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int64_t slot = p.slots[i];
+  if (slot < 0 || slot >= p.num_pages * kPageTokens) return;   // skipped (whole workgroup)
+  const int64_t page = slot / kPageTokens;
+  const int o = (int)(slot % kPageTokens);
+  const TIn* krow = reinterpret_cast<const TIn*>(p.k) + (i * p.heads + h) * kHeadDim;
+  if (wave == 4) {
+    const float2 v = load_pair<TIn>(reinterpret_cast<const TIn*>(p.v) + (i * p.heads + h) * kHeadDim, lane);
+    small_quantize_store<KSEL>(v.x, v.y, true, page, o, h, lane, p);
+  } else if (p.t != nullptr) {
+    // rows c = 32 wave .. 32 wave + 31: k'[2l..2l+1] partial = sum_c k[c] T[c][2l..2l+1]
+    const TIn* th = reinterpret_cast<const TIn*>(p.t) + (int64_t)h * kHeadDim * kHeadDim;
+    float2 tv[32];
+#pragma unroll
+    for (int c = 0; c < 32; ++c) tv[c] = load_pair<TIn>(th + (32 * wave + c) * kHeadDim, lane);
+    float a = 0.0f, b = 0.0f;
+#pragma unroll
+    for (int c = 0; c < 32; ++c) {
+      const float kc = Elem<TIn>::get(krow, 32 * wave + c);
+      a = __builtin_fmaf(kc, tv[c].x, a);
+      b = __builtin_fmaf(kc, tv[c].y, b);
+    }
+    part[wave][2 * lane] = a;
+    part[wave][2 * lane + 1] = b;
+  }
+  __syncthreads();
+  if (wave == 0) {
+    float a, b;
+    if (p.t != nullptr) {
+      a = ((part[0][2 * lane] + part[1][2 * lane]) + part[2][2 * lane]) + part[3][2 * lane];
+      b = ((part[0][2 * lane + 1] + part[1][2 * lane + 1]) + part[2][2 * lane + 1]) + part[3][2 * lane + 1];
+    } else {
+      const float2 v = load_pair<TIn>(krow, lane);
+      a = v.x;
+      b = v.y;
+    }
+    small_quantize_store<KSEL>(a, b, false, page, o, h, lane, p);
+  }
+}
+
 template <typename TIn>
 hipError_t launch_typed(const AppendParams& p, hipStream_t stream) {
-  if (p.n <= kSmallMaxTokens) {
-    hipLaunchKernelGGL((append_small_kernel<TIn>), dim3((unsigned)p.n, (unsigned)p.heads), dim3(128), 0, stream, p);
-    return hipGetLastError();
-  }
-  dim3 grid((unsigned)((p.n + kBlockTokens - 1) / kBlockTokens), (unsigned)p.heads, 2u);
-  dim3 block(256);
   // order statistics needed from the sorted group: ilo, ilo+1, ihi, ihi+1
   auto reach = [](int r) { return r < kHeadDim / 2 ? r + 1 : kHeadDim - r; };
   int need = 0;
@@ -692,6 +771,13 @@ hipError_t launch_typed(const AppendParams& p, hipStream_t stream) {
                        p.ihi + 1 < kHeadDim ? p.ihi + 1 : kHeadDim - 1};
     for (int r : rs) need = reach(r) > need ? reach(r) : need;
   }
+  if (p.n <= kSmallMaxTokens) {
+    const dim3 grid((unsigned)p.n, (unsigned)p.heads), block(64 * kSmallWaves);
+    if (need <= 3) hipLaunchKernelGGL((append_small_kernel<TIn, 3>), grid, block, 0, stream, p);
+    else hipLaunchKernelGGL((append_small_kernel<TIn, 0>), grid, block, 0, stream, p);
+    return hipGetLastError();
+  }
+  const dim3 grid((unsigned)((p.n + kBlockTokens - 1) / kBlockTokens), (unsigned)p.heads, 2u), block(256);
   if (need <= 3) {
     hipLaunchKernelGGL((append_kernel<TIn, 3>), grid, block, 0, stream, p);
   } else if (need <= 8) {
