@@ -1,18 +1,20 @@
 """Benchmark of one decode step of the quantized-KV-cache hot path on one MI355X.
 
-A step is the whole hot path over one batch: kvq_quantize_append of the batch's new
-tokens (one per sequence, dense key transform on the matrix cores, 2-bit percentile
-codes) followed by kvq_decode_attn over every cached token.  Default workload: the
-Qwen3-8B-shaped layer (32 query heads, 8 KV heads, head_dim 128) at batch 64 x 16384
-cached tokens, 2-bit K and V, synthetic Sigma-model data, caches resident in HBM.
+A step is the whole hot path over one batch: the batch's new tokens (one per sequence) are
+transformed, clipped, quantized to 2-bit percentile codes and packed into the cache, and
+every sequence is decoded over its whole cache, new token included: one kvq_decode_step
+launch.  Default workload: the Qwen3-8B-shaped layer (32 query heads, 8 KV heads, head_dim
+128) at batch 64 x 16384 cached tokens, 2-bit K and V, synthetic Sigma-model data, caches
+resident in HBM.
 
 Each timed region is one replay of a HIP graph of K consecutive steps captured from the
 library calls (the calls launch on torch's current stream, which the capture records), so
-host-side call cost does not pace the GPU.  Prints one JSON line.  `value` is cached tokens read per second (batch x
-context per step time).  `roofline` is for the decode kernel: algorithmic bytes per launch
-over its average launch time (HIP events around replays of a decode-only graph on the
-launch stream) against 8 TB/s.  `cpu_baseline`
-is the CPU oracle's decode timed on a bounded sample of sequences of the same shape.
+host-side call cost does not pace the GPU.  Prints one JSON line.  `value` is cached
+tokens read per second (batch x context per step time).  `roofline` is for the step's
+dominant kernel, the decode: algorithmic bytes per launch over its average launch time
+(HIP events on the launch stream around the timed replay of a decode-only graph) against
+8 TB/s.  `cpu_baseline` is the CPU oracle's decode timed on a bounded sample of sequences
+of the same shape.
 """
 from __future__ import annotations
 
@@ -94,11 +96,12 @@ def setup_decode(w, torch, api, calib, synth, dev):
 
 
 def time_steps(w, s, torch, api, steps, warmup):
-    """Times the step as one HIP-graph replay of `steps` consecutive steps (captured from the
+    """Times the step, kvq_decode_step (the batch's new tokens appended, then every sequence
+    decoded), as one HIP-graph replay of `steps` consecutive steps (captured from the
     library calls, which launch on torch's current stream), after one replay of a graph of
     `warmup` steps, so the host's per-call and per-replay cost does not pace the GPU.  HIP
-    events on the launch stream bracket the timed replay.  Graphs holding only the append
-    or only the decode calls, timed the same way, give each call's average."""
+    events on the launch stream bracket the timed replay.  The append and the decode kernel
+    alone are timed the same way.  Returns ms per step of each."""
 
     def append():
         api.kvq_quantize_append(s["cache"], s["knew"], s["vnew"], s["new_slots"], t_k=s["t_k"])
@@ -108,8 +111,8 @@ def time_steps(w, s, torch, api, steps, warmup):
                             out=s["out"], workspace=s["ws"])
 
     def step():
-        append()
-        decode()
+        api.kvq_decode_step(s["cache"], s["q"], s["knew"], s["vnew"], s["new_slots"], s["bt"], s["seq"],
+                            w.seq_len, t_k=s["t_k"], t_k_inv_t=s["t_inv"], out=s["out"], workspace=s["ws"])
 
     step()                                   # first call (library load) outside the graphs
     torch.cuda.synchronize()
@@ -140,7 +143,7 @@ def time_steps(w, s, torch, api, steps, warmup):
     ms_step, wall_step = timed(step)
     ms_app, _ = timed(append)
     ms_dec, _ = timed(decode)
-    return ms_step, wall_step, ms_app, ms_dec
+    return dict(step=ms_step, wall=wall_step, append=ms_app, decode=ms_dec)
 
 
 def time_prefill(w, torch, api, calib, synth, dev, reps=20):
@@ -163,6 +166,24 @@ def time_prefill(w, torch, api, calib, synth, dev, reps=20):
     by = append_algorithmic_bytes(w, n)
     return {"workload": w.name, "us": ms * 1e3, "GB_s": by / (ms * 1e-3) / 1e9,
             "frac": by / (ms * 1e-3) / HBM_PEAK, "algorithmic_bytes": by}
+
+
+def step_traffic_bytes():
+    """HBM bytes per decode launch from the committed rocprofv3 counter summary
+    (FETCH_SIZE + WRITE_SIZE scaled by a plain copy's reading), or None when that summary
+    is missing or was taken on other kernel sources than the ones built here."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "decode_qwen3-8b-b64-16k_hbm_counters.md")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    fields = dict(line.split(":", 1) for line in text.splitlines() if line.startswith(("sources_sha256:", "traffic_bytes:")))
+    h = hashlib.sha256()
+    for f in ("kvq_decode.hip", "kvq_device.h", "kvq_internal.h"):
+        h.update(open(os.path.join(ROOT, "decode_attention_kvq_amd", "csrc", f), "rb").read())
+    if fields.get("sources_sha256", "").strip() != h.hexdigest():
+        return None
+    return float(fields["traffic_bytes"])
 
 
 def cpu_baseline(w, seconds):
@@ -204,30 +225,30 @@ def main():
     dev = torch.device("cuda:0")
     w = synth.WORKLOADS[args.workload]
     s = setup_decode(w, torch, api, calib, synth, dev)
-    ms_step, wall_step, ms_app, ms_dec = time_steps(w, s, torch, api, args.steps, args.warmup)
+    t = time_steps(w, s, torch, api, args.steps, args.warmup)
     cached = w.batch * w.seq_len
     dbytes = decode_algorithmic_bytes(w, w.batch, w.seq_len)
-    achieved = dbytes / (ms_dec * 1e-3)
+    achieved = dbytes / (t["decode"] * 1e-3)
     rec = {
         "metric": "decode-attn cached tokens/s + HBM GB/s (% of peak), 2-bit, batch x 16K ctx",
-        "value": cached / (ms_step * 1e-3),
+        "value": cached / (t["step"] * 1e-3),
         "unit": "cached tokens/s",
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
-        "ms_per_step": ms_step,
+        "ms_per_step": t["step"],
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "u2 codes, f16 matrix-core products, f32 accumulate",
+        "dtype": "u2 codes; fp4 x fp6 (scores) and f16 (P.V) matrix-core products, f32 accumulate",
         "data": "synthetic",
         "config": {"workload": w.name, "batch": w.batch, "seq_len": w.seq_len, "heads_q": w.heads_q,
                    "heads_kv": w.heads_kv, "head_dim": 128, "bits_k": w.bits_k, "bits_v": w.bits_v,
                    "quantizer": w.quantizer, "page_tokens": 64, "parallelism": "single GPU"},
         "roofline": {"bound": "hbm", "achieved": achieved / 1e9, "peak": HBM_PEAK / 1e9, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK, "traffic": None,
-                     "kernel": "kvq decode (main + split combine)", "algorithmic_bytes": dbytes,
-                     "avg_us": ms_dec * 1e3},
-        "wall_ms_per_step": wall_step,
-        "append_us": ms_app * 1e3,
-        "decode_GB_s": achieved / 1e9,
-        "decode_tokens_per_s": cached / (ms_dec * 1e-3),
+                     "frac": achieved / HBM_PEAK, "traffic": step_traffic_bytes(),
+                     "kernel": "decode_kernel (kvq_decode_attn)", "algorithmic_bytes": dbytes,
+                     "avg_us": t["decode"] * 1e3},
+        "wall_ms_per_step": t["wall"],
+        "append_us": t["append"] * 1e3,
+        "decode_us": t["decode"] * 1e3,
+        "decode_tokens_per_s": cached / (t["decode"] * 1e-3),
     }
     del s
     torch.cuda.empty_cache()
@@ -236,11 +257,12 @@ def main():
         for name in ("qwen3-8b-b1-16k", "long-b16-128k-quest"):
             w2 = synth.WORKLOADS[name]
             s2 = setup_decode(w2, torch, api, calib, synth, dev)
-            _, _, _, md = time_steps(w2, s2, torch, api, 20, 10)
-            by = decode_algorithmic_bytes(w2, w2.batch, w2.seq_len)
-            extra[name] = {"decode_us": md * 1e3, "GB_s": by / (md * 1e-3) / 1e9,
-                           "frac": by / (md * 1e-3) / HBM_PEAK,
-                           "tokens_per_s": w2.batch * w2.seq_len / (md * 1e-3)}
+            t2 = time_steps(w2, s2, torch, api, 20, 10)
+            dby = decode_algorithmic_bytes(w2, w2.batch, w2.seq_len)
+            extra[name] = {"step_us": t2["step"] * 1e3, "tokens_per_s": w2.batch * w2.seq_len / (t2["step"] * 1e-3),
+                           "append_us": t2["append"] * 1e3, "decode_us": t2["decode"] * 1e3,
+                           "decode_GB_s": dby / (t2["decode"] * 1e-3) / 1e9,
+                           "decode_frac": dby / (t2["decode"] * 1e-3) / HBM_PEAK}
             del s2
             torch.cuda.empty_cache()
         for name in ("prefill-8x32k-4bit", "prefill-8x32k-2bit"):

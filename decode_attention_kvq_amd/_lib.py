@@ -15,7 +15,7 @@ KVQ_OK = 0
 STATUS_NAMES = {0: "KVQ_OK", -1: "KVQ_ERR_INVALID_ARG", -2: "KVQ_ERR_UNSUPPORTED",
                 -3: "KVQ_ERR_WORKSPACE", -4: "KVQ_ERR_HIP"}
 EXPORTS = ("kvq_block_bytes", "kvq_quantize_append", "kvq_decode_workspace_bytes",
-           "kvq_decode_attn", "kvq_dequant", "kvq_status_string", "kvq_last_error")
+           "kvq_decode_attn", "kvq_decode_step", "kvq_dequant", "kvq_status_string", "kvq_last_error")
 
 
 class KvqCacheDesc(C.Structure):
@@ -52,6 +52,8 @@ def load():
     L.kvq_decode_workspace_bytes.argtypes = [D, i32, i32, i32]
     L.kvq_decode_attn.restype = i32
     L.kvq_decode_attn.argtypes = [D, P, i32, i32, i32, P, P, i32, P, i32, f32, P, P, sz, P]
+    L.kvq_decode_step.restype = i32
+    L.kvq_decode_step.argtypes = [D, P, P, P, i32, i32, i32, P, P, i32, P, P, i32, P, i32, f32, P, P, sz, P]
     L.kvq_dequant.restype = i32
     L.kvq_dequant.argtypes = [D, i32, P, i64, P, P]
     L.kvq_status_string.restype = C.c_char_p

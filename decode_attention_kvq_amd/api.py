@@ -3,7 +3,7 @@
 Argument marshalling only: tensors supply device pointers, the current torch stream
 supplies the hipStream_t, and every step of the computation runs in the HIP kernels of
 libkvq.so.  Function names follow the C entry points (kvq_quantize_append,
-kvq_decode_attn, kvq_dequant).
+kvq_decode_attn, kvq_decode_step, kvq_dequant).
 """
 from __future__ import annotations
 
@@ -111,6 +111,38 @@ def kvq_decode_attn(cache: KVCache, q: torch.Tensor, block_table: torch.Tensor, 
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     d = cache.desc()
     check(load().kvq_decode_attn(C.byref(d), _ptr(q), _DTYPES[q.dtype], B, Hq, _ptr(t_k_inv_t),
+                                 _ptr(block_table), block_table.shape[1], _ptr(seq_lens), max_seq_len,
+                                 float(sm_scale), _ptr(out), _ptr(workspace), ws_bytes, _stream(stream)))
+    return out
+
+
+def kvq_decode_step(cache: KVCache, q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor,
+                    new_slots: torch.Tensor, block_table: torch.Tensor, seq_lens: torch.Tensor,
+                    max_seq_len: int, t_k: torch.Tensor | None = None,
+                    t_k_inv_t: torch.Tensor | None = None, sm_scale: float | None = None,
+                    out: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
+                    stream=None) -> torch.Tensor:
+    """Append each sequence's new token (k_new, v_new: [B, kv_heads, 128]; new_slots: [B]
+    int64, the slot of position seq_lens[b]-1) and decode, in one launch.  Returns out."""
+    _dev(q, "q"); _dev(k_new, "k_new", q.dtype); _dev(v_new, "v_new", q.dtype)
+    _dev(new_slots, "new_slots", torch.int64); _dev(t_k, "t_k", q.dtype)
+    _dev(block_table, "block_table", torch.int32); _dev(seq_lens, "seq_lens", torch.int32)
+    _dev(t_k_inv_t, "t_k_inv_t", torch.float32)
+    B, Hq, _ = q.shape
+    assert k_new.shape == (B, cache.num_kv_heads, HEAD_DIM) and v_new.shape == k_new.shape
+    assert new_slots.shape == (B,)
+    if out is None:
+        out = torch.empty((B, Hq, HEAD_DIM), dtype=torch.float32, device=q.device)
+    _dev(out, "out", torch.float32)
+    if sm_scale is None:
+        sm_scale = 1.0 / math.sqrt(HEAD_DIM)
+    need = decode_workspace_bytes(cache, B, Hq, max_seq_len)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    d = cache.desc()
+    check(load().kvq_decode_step(C.byref(d), _ptr(q), _ptr(k_new), _ptr(v_new), _DTYPES[q.dtype], B, Hq,
+                                 _ptr(new_slots), _ptr(t_k), _DTYPES[q.dtype], _ptr(t_k_inv_t),
                                  _ptr(block_table), block_table.shape[1], _ptr(seq_lens), max_seq_len,
                                  float(sm_scale), _ptr(out), _ptr(workspace), ws_bytes, _stream(stream)))
     return out

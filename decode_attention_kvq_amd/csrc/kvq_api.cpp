@@ -80,6 +80,62 @@ WorkspaceLayout workspace_layout(int batch, int heads_q, int chunks) {
   return w;
 }
 
+kvq::AppendParams append_params(const kvq_cache_desc* cache, const void* k, const void* v, const int64_t* slots,
+                                int64_t n_tokens, const void* t_k) {
+  kvq::AppendParams p{};
+  p.k = k; p.v = v; p.slots = slots; p.t = t_k;
+  p.kpool = static_cast<uint8_t*>(cache->k_pages);
+  p.vpool = static_cast<uint8_t*>(cache->v_pages);
+  p.n = n_tokens; p.num_pages = cache->num_pages; p.heads = cache->num_kv_heads;
+  p.bits_k = cache->bits_k; p.bits_v = cache->bits_v;
+  p.quant_k = cache->quant_k; p.quant_v = cache->quant_v;
+  percentile_position(cache->p_lo, &p.ilo, &p.flo);
+  percentile_position(cache->p_hi, &p.ihi, &p.fhi);
+  p.alpha_k = cache->alpha_k; p.alpha_v = cache->alpha_v;
+  return p;
+}
+
+// Checks and fills the decode launch; shared by kvq_decode_attn and kvq_decode_step.
+kvq_status decode_params(const kvq_cache_desc* cache, const void* q, kvq_dtype q_dtype, int32_t batch,
+                         int32_t num_q_heads, const float* t_k_inv_t, const int32_t* block_table,
+                         int32_t max_pages, const int32_t* seq_lens, int32_t max_seq_len, float sm_scale,
+                         float* out, void* workspace, size_t workspace_bytes, kvq::DecodeParams* pp) {
+  if (batch < 0) return fail(KVQ_ERR_INVALID_ARG, "batch must be >= 0");
+  kvq_status s = check_cache(cache, batch > 0, batch > 0);
+  if (s != KVQ_OK) return s;
+  if (num_q_heads < 1 || num_q_heads % cache->num_kv_heads != 0)
+    return fail(KVQ_ERR_INVALID_ARG, "num_q_heads must be a positive multiple of num_kv_heads");
+  const int group = num_q_heads / cache->num_kv_heads;
+  if (group > 16) return fail(KVQ_ERR_UNSUPPORTED, "at most 16 query heads per KV head");
+  if (!valid_dtype(q_dtype)) return fail(KVQ_ERR_INVALID_ARG, "unknown query dtype");
+  if (max_seq_len < 0 || max_pages < 0) return fail(KVQ_ERR_INVALID_ARG, "max_seq_len and max_pages must be >= 0");
+  if ((int64_t)max_pages * 64 < (int64_t)max_seq_len)
+    return fail(KVQ_ERR_INVALID_ARG, "max_pages*64 must cover max_seq_len");
+  if (!std::isfinite(sm_scale)) return fail(KVQ_ERR_INVALID_ARG, "sm_scale must be finite");
+  if (batch == 0) return KVQ_OK;
+  if (batch > 65535) return fail(KVQ_ERR_UNSUPPORTED, "batch must be <= 65535");
+  if (!q || !block_table || !seq_lens || !out)
+    return fail(KVQ_ERR_INVALID_ARG, "q, block_table, seq_lens and out must be non-null");
+  const kvq::DecodeSplit sp = kvq::decode_split(batch, cache->num_kv_heads, max_seq_len);
+  const WorkspaceLayout wl = workspace_layout(batch, num_q_heads, sp.chunks);
+  if (wl.total > 0 && (!workspace || workspace_bytes < wl.total))
+    return fail(KVQ_ERR_WORKSPACE, "workspace smaller than kvq_decode_workspace_bytes()");
+  if (cache->num_pages < 1) return fail(KVQ_ERR_INVALID_ARG, "num_pages must be >= 1");
+  kvq::DecodeParams& p = *pp;
+  p = kvq::DecodeParams{};
+  p.kpool = static_cast<const uint8_t*>(cache->k_pages);
+  p.vpool = static_cast<const uint8_t*>(cache->v_pages);
+  p.q = q; p.tinv = t_k_inv_t; p.block_table = block_table; p.seq_lens = seq_lens; p.out = out;
+  char* ws = static_cast<char*>(workspace);
+  p.ws_o = wl.o_bytes ? reinterpret_cast<float*>(ws) : nullptr;
+  p.ws_ml = wl.ml_bytes ? reinterpret_cast<float*>(ws + wl.o_bytes) : nullptr;
+  p.batch = batch; p.heads_q = num_q_heads; p.heads_kv = cache->num_kv_heads; p.group = group;
+  p.gpad = kvq::decode_group_pad(group);
+  p.max_pages = max_pages; p.num_pages = cache->num_pages; p.pages_per_wave = sp.pages_per_wave; p.chunks = sp.chunks;
+  p.score_scale = sm_scale * 1.4426950408889634f;
+  return KVQ_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -116,16 +172,7 @@ kvq_status kvq_quantize_append(const kvq_cache_desc* cache, const void* k, const
   if (n_tokens == 0) return KVQ_OK;
   if (!k || !v || !slot_mapping) return fail(KVQ_ERR_INVALID_ARG, "k, v and slot_mapping must be non-null");
   if ((n_tokens + 127) / 128 > 0x7FFFFFFFLL) return fail(KVQ_ERR_UNSUPPORTED, "too many tokens");
-  kvq::AppendParams p{};
-  p.k = k; p.v = v; p.slots = slot_mapping; p.t = t_k;
-  p.kpool = static_cast<uint8_t*>(cache->k_pages);
-  p.vpool = static_cast<uint8_t*>(cache->v_pages);
-  p.n = n_tokens; p.num_pages = cache->num_pages; p.heads = cache->num_kv_heads;
-  p.bits_k = cache->bits_k; p.bits_v = cache->bits_v;
-  p.quant_k = cache->quant_k; p.quant_v = cache->quant_v;
-  percentile_position(cache->p_lo, &p.ilo, &p.flo);
-  percentile_position(cache->p_hi, &p.ihi, &p.fhi);
-  p.alpha_k = cache->alpha_k; p.alpha_v = cache->alpha_v;
+  const kvq::AppendParams p = append_params(cache, k, v, slot_mapping, n_tokens, t_k);
   return hip_status(kvq::launch_append(p, (int)in_dtype, static_cast<hipStream_t>(stream)));
 }
 
@@ -141,40 +188,37 @@ kvq_status kvq_decode_attn(const kvq_cache_desc* cache, const void* q, kvq_dtype
                            int32_t max_pages, const int32_t* seq_lens, int32_t max_seq_len, float sm_scale,
                            float* out, void* workspace, size_t workspace_bytes, void* stream) {
   g_last_error.clear();
-  if (batch < 0) return fail(KVQ_ERR_INVALID_ARG, "batch must be >= 0");
-  kvq_status s = check_cache(cache, batch > 0, batch > 0);
-  if (s != KVQ_OK) return s;
-  if (num_q_heads < 1 || num_q_heads % cache->num_kv_heads != 0)
-    return fail(KVQ_ERR_INVALID_ARG, "num_q_heads must be a positive multiple of num_kv_heads");
-  const int group = num_q_heads / cache->num_kv_heads;
-  if (group > 16) return fail(KVQ_ERR_UNSUPPORTED, "at most 16 query heads per KV head");
-  if (!valid_dtype(q_dtype)) return fail(KVQ_ERR_INVALID_ARG, "unknown query dtype");
-  if (max_seq_len < 0 || max_pages < 0) return fail(KVQ_ERR_INVALID_ARG, "max_seq_len and max_pages must be >= 0");
-  if ((int64_t)max_pages * 64 < (int64_t)max_seq_len)
-    return fail(KVQ_ERR_INVALID_ARG, "max_pages*64 must cover max_seq_len");
-  if (!std::isfinite(sm_scale)) return fail(KVQ_ERR_INVALID_ARG, "sm_scale must be finite");
-  if (batch == 0) return KVQ_OK;
-  if (batch > 65535) return fail(KVQ_ERR_UNSUPPORTED, "batch must be <= 65535");
-  if (!q || !block_table || !seq_lens || !out)
-    return fail(KVQ_ERR_INVALID_ARG, "q, block_table, seq_lens and out must be non-null");
-  const kvq::DecodeSplit sp = kvq::decode_split(batch, cache->num_kv_heads, max_seq_len);
-  const WorkspaceLayout wl = workspace_layout(batch, num_q_heads, sp.chunks);
-  if (wl.total > 0 && (!workspace || workspace_bytes < wl.total))
-    return fail(KVQ_ERR_WORKSPACE, "workspace smaller than kvq_decode_workspace_bytes()");
-  if (cache->num_pages < 1) return fail(KVQ_ERR_INVALID_ARG, "num_pages must be >= 1");
-  kvq::DecodeParams p{};
-  p.kpool = static_cast<const uint8_t*>(cache->k_pages);
-  p.vpool = static_cast<const uint8_t*>(cache->v_pages);
-  p.q = q; p.tinv = t_k_inv_t; p.block_table = block_table; p.seq_lens = seq_lens; p.out = out;
-  char* ws = static_cast<char*>(workspace);
-  p.ws_o = wl.o_bytes ? reinterpret_cast<float*>(ws) : nullptr;
-  p.ws_ml = wl.ml_bytes ? reinterpret_cast<float*>(ws + wl.o_bytes) : nullptr;
-  p.batch = batch; p.heads_q = num_q_heads; p.heads_kv = cache->num_kv_heads; p.group = group;
-  p.gpad = kvq::decode_group_pad(group);
-  p.max_pages = max_pages; p.num_pages = cache->num_pages; p.pages_per_wave = sp.pages_per_wave; p.chunks = sp.chunks;
-  p.score_scale = sm_scale * 1.4426950408889634f;
+  kvq::DecodeParams p;
+  kvq_status s = decode_params(cache, q, q_dtype, batch, num_q_heads, t_k_inv_t, block_table, max_pages, seq_lens,
+                               max_seq_len, sm_scale, out, workspace, workspace_bytes, &p);
+  if (s != KVQ_OK || batch == 0) return s;
   return hip_status(kvq::launch_decode(p, cache->bits_k, cache->bits_v, (int)q_dtype,
                                        static_cast<hipStream_t>(stream)));
+}
+
+kvq_status kvq_decode_step(const kvq_cache_desc* cache, const void* q, const void* k_new, const void* v_new,
+                           kvq_dtype dtype, int32_t batch, int32_t num_q_heads, const int64_t* new_slots,
+                           const void* t_k, kvq_dtype t_dtype, const float* t_k_inv_t,
+                           const int32_t* block_table, int32_t max_pages, const int32_t* seq_lens,
+                           int32_t max_seq_len, float sm_scale, float* out, void* workspace,
+                           size_t workspace_bytes, void* stream) {
+  g_last_error.clear();
+  kvq::DecodeParams p;
+  kvq_status s = decode_params(cache, q, dtype, batch, num_q_heads, t_k_inv_t, block_table, max_pages, seq_lens,
+                               max_seq_len, sm_scale, out, workspace, workspace_bytes, &p);
+  if (s != KVQ_OK) return s;
+  if ((s = check_quantizer(cache->quant_k, cache->alpha_k, cache->p_lo, cache->p_hi)) != KVQ_OK) return s;
+  if ((s = check_quantizer(cache->quant_v, cache->alpha_v, cache->p_lo, cache->p_hi)) != KVQ_OK) return s;
+  if (t_k && t_dtype != dtype) return fail(KVQ_ERR_UNSUPPORTED, "t_dtype must equal dtype");
+  if (batch == 0) return KVQ_OK;
+  if (!k_new || !v_new || !new_slots) return fail(KVQ_ERR_INVALID_ARG, "k_new, v_new and new_slots must be non-null");
+  // two launches in stream order: the append, then the decode that reads it.  (Writing the
+  // new token inside the decode kernel, by the workgroup that reads the last page, measured
+  // slower: its latency lands at the start of every workgroup, before the page stream.)
+  const kvq::AppendParams a = append_params(cache, k_new, v_new, new_slots, batch, t_k);
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  if ((s = hip_status(kvq::launch_append(a, (int)dtype, st))) != KVQ_OK) return s;
+  return hip_status(kvq::launch_decode(p, cache->bits_k, cache->bits_v, (int)dtype, st));
 }
 
 kvq_status kvq_dequant(const kvq_cache_desc* cache, int32_t which, const int64_t* slots, int64_t n_tokens,

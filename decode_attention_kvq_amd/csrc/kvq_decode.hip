@@ -268,6 +268,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
   const int pg0 = wv * p.pages_per_wave;
   const int np = max(0, min(pg0 + p.pages_per_wave, npages) - pg0);
   const int32_t* bt = p.block_table + (int64_t)b * p.max_pages;
+
   // the wave's page ids (at most 64) sit one per lane; the walk reads them with readlane
   int my_page = -1;                        // validated after the prologue loads are out
   if (np > 0) my_page = bt[pg0 + min(lane, np - 1)];
@@ -473,6 +474,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
   }
   const float F = gq < G ? hconst[2 * gq + 1] : 1.0f;                  // score = F * x'
   const float qsf = gq < G ? hconst[2 * gq] / hconst[2 * gq + 1] : 0.0f;
+
 
   // per (accumulator a, row r): token u = 4*(a*NB + beta) + r of this lane group
   f32x4 acc_o[8];

@@ -23,6 +23,20 @@ struct AppendParams {
   float alpha_k, alpha_v;
 };
 
+// Width of the insertion networks that hold every order statistic the percentile clip
+// needs (positions ilo, ilo+1, ihi, ihi+1 of 128); 0 means a full sort.
+__host__ __device__ inline int select_width(const AppendParams& p) {
+  constexpr int kHeadDim = 128;
+  if (p.quant_k != 0 && p.quant_v != 0) return 3;
+  auto reach = [](int r) { return r < kHeadDim / 2 ? r + 1 : kHeadDim - r; };
+  const int rs[4] = {p.ilo, p.ilo + 1 < kHeadDim ? p.ilo + 1 : kHeadDim - 1, p.ihi,
+                     p.ihi + 1 < kHeadDim ? p.ihi + 1 : kHeadDim - 1};
+  int need = 0;
+  for (int r : rs) need = reach(r) > need ? reach(r) : need;
+  return need <= 3 ? 3 : (need <= 8 ? 8 : 0);
+}
+
+
 struct DecodeParams {
   const uint8_t* kpool;
   const uint8_t* vpool;

@@ -102,8 +102,10 @@ size_t kvq_block_bytes(int32_t bits);
  *   slot_mapping  device, [n_tokens] int64; slot of each token.  Slots must be
  *                 distinct; a slot < 0 or >= num_pages*64 is skipped (nothing written).
  *   t_k           device, [num_kv_heads][128][128] row-major, k' = k . T_K; or NULL for
- *                 the identity.  t_dtype must equal in_dtype (bf16 and f16 inputs use
- *                 matrix cores with fp32 accumulation; f32 uses fp32 arithmetic).
+ *                 the identity.  t_dtype must equal in_dtype.  Batches of up to 512
+ *                 tokens transform with fp32 fused multiply-adds (four partial sums over
+ *                 32 rows of T, added in order); larger bf16/f16 batches use the matrix
+ *                 cores with fp32 accumulation, f32 batches fp32 arithmetic.
  * Bits of a block not belonging to the written tokens are preserved, so tokens may be
  * appended one at a time into partly filled pages. */
 kvq_status kvq_quantize_append(const kvq_cache_desc* cache, const void* k, const void* v,
@@ -137,6 +139,31 @@ size_t kvq_decode_workspace_bytes(const kvq_cache_desc* cache, int32_t batch,
  *                share a workspace must be ordered (same stream). */
 kvq_status kvq_decode_attn(const kvq_cache_desc* cache, const void* q, kvq_dtype q_dtype,
                            int32_t batch, int32_t num_q_heads, const float* t_k_inv_t,
+                           const int32_t* block_table, int32_t max_pages,
+                           const int32_t* seq_lens, int32_t max_seq_len, float sm_scale,
+                           float* out, void* workspace, size_t workspace_bytes,
+                           void* stream);
+
+/* One decode step with the step's new tokens: for every sequence b, the key and value of
+ * its new token (all KV heads) are encoded exactly as kvq_quantize_append encodes them and
+ * written at new_slots[b]; then sequence b is read as by kvq_decode_attn over positions
+ * [0, seq_lens[b]), the new token included.  This is the write path of "WUSH-KV: KV Cache
+ * Quantization with Data-Adaptive Transforms" §4.2/§4.3 followed by its read path (§4.1,
+ * §4.2) as one call (two kernels in stream order on `stream`).
+ *   q, k_new, v_new  device, [batch][num_q_heads][128] and [batch][num_kv_heads][128] of
+ *                 dtype (post-RoPE query and key; the value in the folded basis).
+ *   new_slots     device, [batch] int64: the slot of position seq_lens[b]-1 of sequence b
+ *                 (page block_table[b][(seq_lens[b]-1)/64], offset (seq_lens[b]-1)%64);
+ *                 < 0 or >= num_pages*64: no new token for that sequence.  Another slot
+ *                 is written, but the output may then miss it.
+ *   t_k           as in kvq_quantize_append (t_dtype must equal dtype); t_k_inv_t,
+ *                 block_table, seq_lens, max_seq_len, sm_scale, out, workspace as in
+ *                 kvq_decode_attn (the workspace size is kvq_decode_workspace_bytes()).
+ * The written bytes equal those of kvq_quantize_append for the same new tokens. */
+kvq_status kvq_decode_step(const kvq_cache_desc* cache, const void* q, const void* k_new,
+                           const void* v_new, kvq_dtype dtype, int32_t batch,
+                           int32_t num_q_heads, const int64_t* new_slots, const void* t_k,
+                           kvq_dtype t_dtype, const float* t_k_inv_t,
                            const int32_t* block_table, int32_t max_pages,
                            const int32_t* seq_lens, int32_t max_seq_len, float sm_scale,
                            float* out, void* workspace, size_t workspace_bytes,

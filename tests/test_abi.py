@@ -133,3 +133,24 @@ def test_dequant_argument_checks(lib):
     assert lib.kvq_dequant(C.byref(d), 2, p, 5, p, None) == -1
     assert lib.kvq_dequant(C.byref(d), 0, None, 5, p, None) == -1
     assert lib.kvq_dequant(C.byref(d), 0, p, 0, p, None) == 0
+
+
+def test_decode_step_argument_checks(lib):
+    d = _desc()
+    p = C.c_void_p(0x10)
+
+    def call(**kw):
+        return lib.kvq_decode_step(
+            C.byref(kw.get("d", d)), kw.get("q", p), kw.get("k", p), kw.get("v", p), kw.get("dt", 1),
+            kw.get("B", 2), kw.get("Hq", 32), kw.get("slots", p), kw.get("t", None), kw.get("tdt", 1), None,
+            kw.get("bt", p), kw.get("mp", 4), kw.get("sl", p), kw.get("msl", 256), kw.get("scale", 0.088),
+            kw.get("out", p), kw.get("ws", None), kw.get("wsb", 0), None)
+    assert call(Hq=30) == -1                    # decode checks apply
+    assert call(mp=3) == -1
+    assert call(B=0) == 0
+    assert call(k=None) == -1                   # the new tokens are required
+    assert call(slots=None) == -1
+    assert call(t=p, tdt=0) == -2               # transform dtype differs from the inputs
+    assert call(d=_desc(p_lo=0.7, p_hi=0.2)) == -1
+    assert call(d=_desc(quant_k=1, alpha_k=-1.0)) == -1
+    assert call(B=1, mp=256, msl=16384) == -3   # split launch without a workspace
