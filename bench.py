@@ -41,6 +41,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--extra", action="store_true", help="also time the other workloads")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
+                    help="only run a plain device copy of BYTES bytes 5 times (the reference kernel "
+                         "whose FETCH_SIZE/WRITE_SIZE readings scale the decode kernel's counters)")
     return ap.parse_args()
 
 
@@ -218,6 +221,15 @@ def main():
               "(the decode path would shard by KV head with no exchange)", file=sys.stderr)
         sys.exit(2)
     import torch
+    if args.copy_calibration:
+        n = args.copy_calibration
+        src = torch.ones(n, dtype=torch.uint8, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes": n, "launches": 5}), flush=True)
+        return
     from decode_attention_kvq_amd import api, calib, synth
     from decode_attention_kvq_amd import build as kbuild
     if not os.path.exists(os.path.join(ROOT, "decode_attention_kvq_amd", "libkvq.so")):
