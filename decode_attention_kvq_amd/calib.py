@@ -1,4 +1,4 @@
-"""Host-side (offline) calibration of the per-KV-head key transform.
+"""Host-side (offline) calibration of the per-KV-head key and value transforms.
 
 Follows "WUSH-KV: KV Cache Quantization with Data-Adaptive Transforms":
   §3    the transform comes from the second-order statistics of both factors of the
@@ -9,6 +9,8 @@ Follows "WUSH-KV: KV Cache Quantization with Data-Adaptive Transforms":
         partner is the query: a key error e moves the logit of query q by q.e, so
         H = sum over the query heads that read the KV head of E[q^T q].
   App. B.2  undamped, the transform minimises tr(T^T M T) tr(T^-1 H T^-T).
+  §4.2  the value transform comes from the values' Gram matrix and the Hessian of the
+        output projection, and is folded into W_V and W_O (no read-time cost).
 
 The formula itself is not printed on the pages; this module uses the closed form that
 has every stated property (balanced: T^T M T and T^-1 H T^-T are both diagonal-equal):
@@ -90,3 +92,43 @@ def calibrate_all_heads(k_cal_heads, q_cal_heads, **kw):
     """Stacks calibrate_key_transform over KV heads: returns ([H,d,d], [H,d,d])."""
     pairs = [calibrate_key_transform(k, q, **kw) for k, q in zip(k_cal_heads, q_cal_heads)]
     return np.stack([p[0] for p in pairs]), np.stack([p[1] for p in pairs])
+
+
+# --------------------------------------------------------------------------------------
+# Value side ("WUSH-KV" §4.2: the value transform is folded into W_V and W_O, so the cache
+# holds v T_V and the attention output stays in that basis until W_O absorbs T_V^-1).
+# --------------------------------------------------------------------------------------
+
+def value_statistics(v_cal: np.ndarray, w_o_blocks: np.ndarray):
+    """Gram matrix of one KV head's values and the Hessian of their product partner.
+
+    v_cal: [N, d] values (before any fold); w_o_blocks: [G, d, d_model], the rows of the
+    output projection that the G query heads reading this KV head multiply.  Head g adds
+    o_g W_O,g to the layer output with o_g a convex combination of value rows, so an error
+    e in a value row moves the output by (p e) W_O,g: the surrogate Hessian is
+    H = sum_g W_O,g W_O,g^T."""
+    v = np.asarray(v_cal, dtype=np.float64)
+    w = np.asarray(w_o_blocks, dtype=np.float64)
+    if w.ndim == 2:
+        w = w[None]
+    gram = np.einsum("nc,nd->cd", v, v) / v.shape[0]
+    hess = np.einsum("gcm,gdm->cd", w, w)
+    return gram, hess
+
+
+def calibrate_value_transform(v_cal: np.ndarray, w_o_blocks: np.ndarray, gamma: float = DEFAULT_GAMMA,
+                              hadamard: bool = True) -> np.ndarray:
+    """T_V [d, d] (fp64) for one KV head: the same construction as the key transform, with
+    the values' Gram matrix and the output projection's Hessian."""
+    return wush(*value_statistics(v_cal, w_o_blocks), gamma=gamma, hadamard=hadamard)
+
+
+def fold_value_transform(w_v: np.ndarray, w_o_blocks: np.ndarray, t_v: np.ndarray):
+    """Folds T_V into the projections: W_V' = W_V T_V (so the cached values are v T_V) and
+    W_O,g' = T_V^-1 W_O,g (so o' W_O,g' = o W_O,g for the transformed-basis output o').
+
+    w_v: [d_model, d]; w_o_blocks: [G, d, d_model].  Returns (W_V', W_O') in fp64."""
+    t = np.asarray(t_v, dtype=np.float64)
+    w_v_f = np.asarray(w_v, dtype=np.float64) @ t
+    w_o_f = np.stack([np.linalg.solve(t, w) for w in np.asarray(w_o_blocks, dtype=np.float64)])
+    return w_v_f, w_o_f
