@@ -68,6 +68,10 @@ def lib():
         L.oracle_dequant.argtypes = [P, i32, i32, i32, P, i64, P]
         L.oracle_decode_attention.argtypes = [P, P, i32, i32, i32, P, i32, i32, P, P, i32, P,
                                               f64, P, P]
+        L.oracle_window_quantized.restype = i64
+        L.oracle_window_quantized.argtypes = [i64, i32, i32, i32]
+        L.oracle_window_attention.argtypes = [P, P, i32, i32, i32, P, i32, i32, P, P, i32, P, i32,
+                                              i32, i32, i32, P, P, i64, f64, P, P]
         _lib = L
     return _lib
 
@@ -212,5 +216,44 @@ def decode_attention(k_pool, v_pool, q, block_table, seq_lens, t_inv_t=None, bit
     lse = np.zeros((B, Hq), np.float64)
     lib().oracle_decode_attention(_p(k_pool), _p(v_pool), H, bits_k, bits_v, _p(q), B, Hq,
                                   _p(tt), _p(bt), bt.shape[1], _p(sl), float(sm_scale),
+                                  _p(out), _p(lse))
+    return (out, lse) if return_lse else out
+
+
+def window_quantized(length: int, sink: int, keep: int, flush: int) -> int:
+    """Full-precision windows ([W] §4.4): positions quantized once a sequence has grown to
+    `length` and every waiting batch of `flush` eligible positions has been quantized.
+    Pinned by hand-worked cases and invariants (tests/test_oracle_window.py)."""
+    return int(lib().oracle_window_quantized(int(length), int(sink), int(keep), int(flush)))
+
+
+def window_attention(k_pool, v_pool, q, block_table, seq_lens, k_fp, v_fp, sink, keep, flush,
+                     pending=0, t_inv_t=None, bits_k=2, bits_v=2, sm_scale=None, return_lse=False):
+    """Attention over a windowed cache ([W] §4.4), fp64 output.
+
+    Positions sink .. sink+Q-1 are read dequantized from the paged cache at index
+    position - sink (with the compensated query); every other position reads k_fp / v_fp
+    [B, fp_len, H, 128] (the stored full-precision values) with the plain query.
+    Q = window_quantized(seq_len - pending).  Pinned against decode_attention when every
+    position is quantized, against plain softmax attention when none is, and against
+    torch fp64 attention over keys mapped back to the original basis when mixed
+    (tests/test_oracle_window.py)."""
+    q = _f32(q)
+    B, Hq, _ = q.shape
+    H = k_pool.shape[1]
+    kf = _f32(k_fp)
+    vf = _f32(v_fp)
+    assert kf.shape[0] == B and kf.shape[2] == H and vf.shape == kf.shape
+    bt = np.ascontiguousarray(block_table, dtype=np.int32)
+    sl = np.ascontiguousarray(seq_lens, dtype=np.int32)
+    assert int(sl.max(initial=0)) <= kf.shape[1]
+    tt = None if t_inv_t is None else _f32(t_inv_t)
+    if sm_scale is None:
+        sm_scale = 1.0 / np.sqrt(HEAD_DIM)
+    out = np.zeros((B, Hq, HEAD_DIM), np.float64)
+    lse = np.zeros((B, Hq), np.float64)
+    lib().oracle_window_attention(_p(k_pool), _p(v_pool), H, bits_k, bits_v, _p(q), B, Hq, _p(tt),
+                                  _p(bt), bt.shape[1], _p(sl), int(pending), int(sink), int(keep),
+                                  int(flush), _p(kf), _p(vf), kf.shape[1], float(sm_scale),
                                   _p(out), _p(lse))
     return (out, lse) if return_lse else out

@@ -448,3 +448,115 @@ void oracle_decode_attention(const uint8_t* k_pool, const uint8_t* v_pool, int k
         free(kd); free(vd); free(s);
     }
 }
+
+/* ------------------------------------------------------------------------- */
+/* Full-precision cache windows ([W] §4.4).                                  */
+/* The first `sink` positions and the newest `keep` positions of a sequence  */
+/* stay in full precision.  A position from `sink` on that has at least      */
+/* `keep` newer positions is eligible; eligible positions are quantized, the */
+/* oldest first, in batches of `flush` whenever at least `flush` of them are */
+/* waiting.  New positions are appended (and read by that step's attention)  */
+/* in full precision before the batches that became eligible are quantized.  */
+/*                                                                           */
+/* Reading taken: the quantized positions of a sequence are stored in the    */
+/* paged cache at index j = position - sink (page block_table[b][j/64]).     */
+/* ------------------------------------------------------------------------- */
+
+/* Number of quantized positions after a sequence has grown, one position at  */
+/* a time, to `length` positions and every waiting batch has been quantized.  */
+int64_t oracle_window_quantized(int64_t length, int sink, int keep, int flush)
+{
+    int64_t quantized_end = sink;             /* positions [sink, quantized_end) are quantized */
+    for (int64_t x = 1; x <= length; ++x) {  /* position x-1 arrives */
+        /* eligible and not yet quantized: [quantized_end, x - keep) */
+        while (x - keep - quantized_end >= flush) quantized_end += flush;
+    }
+    return quantized_end - sink;
+}
+
+/* Decode attention over a windowed cache: one exact two-pass softmax over    */
+/* all seq_lens[b] positions of sequence b, where                             */
+/*   quantized positions p (sink <= p < sink + Q) read key k'_j and value v_j */
+/*     dequantized from the paged cache at j = p - sink and use the          */
+/*     compensated query q' = q T^-T (as oracle_decode_attention);            */
+/*   every other position reads its full-precision key and value from       */
+/*     k_fp / v_fp ([batch][fp_len][kv_heads][128], position-major) with the  */
+/*     plain query q (no transform on either side).                           */
+/* Q = oracle_window_quantized(seq_lens[b] - pending): `pending` positions    */
+/* were appended since the last quantization (1 for a decode step, whose     */
+/* attention runs before its flush; 0 for a read after the flush).           */
+/* out: [batch][heads_q][128] fp64; lse (optional) natural log of sum exp(s). */
+/* ------------------------------------------------------------------------- */
+void oracle_window_attention(const uint8_t* k_pool, const uint8_t* v_pool, int kv_heads,
+                             int bits_k, int bits_v, const float* q, int batch, int heads_q,
+                             const float* t_inv_t, const int32_t* block_table, int max_pages,
+                             const int32_t* seq_lens, int pending, int sink, int keep, int flush,
+                             const float* k_fp, const float* v_fp, int64_t fp_len,
+                             double sm_scale, double* out, double* lse)
+{
+    int group = heads_q / kv_heads;
+    uint8_t codes[HEAD_DIM];
+    for (int b = 0; b < batch; ++b) {
+        int64_t n = seq_lens[b];
+        int64_t x = n - pending > 0 ? n - pending : 0;
+        int64_t nq = oracle_window_quantized(x, sink, keep, flush);
+        double* kd = (double*)malloc(((size_t)n + 1) * HEAD_DIM * sizeof(double));
+        double* vd = (double*)malloc(((size_t)n + 1) * HEAD_DIM * sizeof(double));
+        int* quantized = (int*)malloc(((size_t)n + 1) * sizeof(int));
+        double* s = (double*)malloc(((size_t)n + 1) * sizeof(double));
+        for (int h = 0; h < kv_heads; ++h) {
+            for (int64_t t = 0; t < n; ++t) {
+                quantized[t] = t >= sink && t < sink + nq;
+                if (quantized[t]) {
+                    int64_t j = t - sink;
+                    int64_t page = block_table[(int64_t)b * max_pages + j / PAGE_TOKENS];
+                    int o = (int)(j % PAGE_TOKENS);
+                    uint16_t s16, z16;
+                    oracle_unpack_token(block_at((uint8_t*)k_pool, page, h, kv_heads, bits_k), 0, bits_k, o,
+                                        codes, &s16, &z16);
+                    float sf = oracle_f16_to_f32(s16), zf = oracle_f16_to_f32(z16);
+                    for (int c = 0; c < HEAD_DIM; ++c) kd[t * HEAD_DIM + c] = fmaf((float)codes[c], sf, zf);
+                    oracle_unpack_token(block_at((uint8_t*)v_pool, page, h, kv_heads, bits_v), 1, bits_v, o,
+                                        codes, &s16, &z16);
+                    sf = oracle_f16_to_f32(s16); zf = oracle_f16_to_f32(z16);
+                    for (int c = 0; c < HEAD_DIM; ++c) vd[t * HEAD_DIM + c] = fmaf((float)codes[c], sf, zf);
+                } else {
+                    const float* kr = k_fp + (((int64_t)b * fp_len + t) * kv_heads + h) * HEAD_DIM;
+                    const float* vr = v_fp + (((int64_t)b * fp_len + t) * kv_heads + h) * HEAD_DIM;
+                    for (int c = 0; c < HEAD_DIM; ++c) { kd[t * HEAD_DIM + c] = kr[c]; vd[t * HEAD_DIM + c] = vr[c]; }
+                }
+            }
+            for (int g = 0; g < group; ++g) {
+                int hq = h * group + g;
+                const float* qr = q + ((int64_t)b * heads_q + hq) * HEAD_DIM;
+                double qp[HEAD_DIM];
+                for (int j = 0; j < HEAD_DIM; ++j) {
+                    if (!t_inv_t) { qp[j] = qr[j]; continue; }
+                    double acc = 0.0;
+                    for (int c = 0; c < HEAD_DIM; ++c)
+                        acc += (double)qr[c] * (double)t_inv_t[((int64_t)h * HEAD_DIM + c) * HEAD_DIM + j];
+                    qp[j] = acc;
+                }
+                double* o = out + ((int64_t)b * heads_q + hq) * HEAD_DIM;
+                for (int j = 0; j < HEAD_DIM; ++j) o[j] = 0.0;
+                if (n == 0) { if (lse) lse[(int64_t)b * heads_q + hq] = -INFINITY; continue; }
+                double m = -INFINITY;
+                for (int64_t t = 0; t < n; ++t) {
+                    double acc = 0.0;
+                    for (int c = 0; c < HEAD_DIM; ++c)
+                        acc += (quantized[t] ? qp[c] : (double)qr[c]) * kd[t * HEAD_DIM + c];
+                    s[t] = sm_scale * acc;
+                    if (s[t] > m) m = s[t];
+                }
+                double l = 0.0;
+                for (int64_t t = 0; t < n; ++t) { s[t] = exp(s[t] - m); l += s[t]; }
+                for (int64_t t = 0; t < n; ++t) {
+                    double p = s[t] / l;
+                    for (int j = 0; j < HEAD_DIM; ++j) o[j] += p * vd[t * HEAD_DIM + j];
+                }
+                if (lse) lse[(int64_t)b * heads_q + hq] = m + log(l);
+            }
+        }
+        free(kd); free(vd); free(quantized); free(s);
+    }
+}
