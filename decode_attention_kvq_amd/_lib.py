@@ -15,7 +15,9 @@ KVQ_OK = 0
 STATUS_NAMES = {0: "KVQ_OK", -1: "KVQ_ERR_INVALID_ARG", -2: "KVQ_ERR_UNSUPPORTED",
                 -3: "KVQ_ERR_WORKSPACE", -4: "KVQ_ERR_HIP"}
 EXPORTS = ("kvq_block_bytes", "kvq_quantize_append", "kvq_decode_workspace_bytes",
-           "kvq_decode_attn", "kvq_decode_step", "kvq_dequant", "kvq_status_string", "kvq_last_error")
+           "kvq_decode_attn", "kvq_decode_step", "kvq_dequant", "kvq_window_bytes", "kvq_window_prefill",
+           "kvq_window_workspace_bytes", "kvq_window_decode_attn", "kvq_window_decode_step",
+           "kvq_status_string", "kvq_last_error")
 
 
 class KvqCacheDesc(C.Structure):
@@ -24,6 +26,11 @@ class KvqCacheDesc(C.Structure):
                 ("quant_v", C.c_int32), ("p_lo", C.c_float), ("p_hi", C.c_float),
                 ("alpha_k", C.c_float), ("alpha_v", C.c_float), ("num_pages", C.c_int64),
                 ("k_pages", C.c_void_p), ("v_pages", C.c_void_p)]
+
+
+class KvqWindowDesc(C.Structure):
+    _fields_ = [("sink", C.c_int32), ("keep", C.c_int32), ("flush", C.c_int32), ("num_rows", C.c_int32),
+                ("dtype", C.c_int32), ("k_win", C.c_void_p), ("v_win", C.c_void_p)]
 
 
 class KvqError(RuntimeError):
@@ -56,6 +63,17 @@ def load():
     L.kvq_decode_step.argtypes = [D, P, P, P, i32, i32, i32, P, P, i32, P, P, i32, P, i32, f32, P, P, sz, P]
     L.kvq_dequant.restype = i32
     L.kvq_dequant.argtypes = [D, i32, P, i64, P, P]
+    W = C.POINTER(KvqWindowDesc)
+    L.kvq_window_bytes.restype = sz
+    L.kvq_window_bytes.argtypes = [D, W]
+    L.kvq_window_prefill.restype = i32
+    L.kvq_window_prefill.argtypes = [D, W, P, P, i32, P, i64, P, i32, P, P, P]
+    L.kvq_window_workspace_bytes.restype = sz
+    L.kvq_window_workspace_bytes.argtypes = [D, W, i32, i32, i32]
+    L.kvq_window_decode_attn.restype = i32
+    L.kvq_window_decode_attn.argtypes = [D, W, P, i32, i32, P, P, i32, P, P, i32, f32, P, P, sz, P]
+    L.kvq_window_decode_step.restype = i32
+    L.kvq_window_decode_step.argtypes = [D, W, P, P, P, i32, i32, P, P, P, i32, P, P, i32, f32, P, P, sz, P]
     L.kvq_status_string.restype = C.c_char_p
     L.kvq_status_string.argtypes = [i32]
     L.kvq_last_error.restype = C.c_char_p

@@ -3,7 +3,8 @@
 Argument marshalling only: tensors supply device pointers, the current torch stream
 supplies the hipStream_t, and every step of the computation runs in the HIP kernels of
 libkvq.so.  Function names follow the C entry points (kvq_quantize_append,
-kvq_decode_attn, kvq_decode_step, kvq_dequant).
+kvq_decode_attn, kvq_decode_step, kvq_dequant, and the full-precision window calls
+kvq_window_prefill, kvq_window_decode_attn, kvq_window_decode_step).
 """
 from __future__ import annotations
 
@@ -12,7 +13,7 @@ import math
 
 import torch
 
-from ._lib import KvqCacheDesc, check, load
+from ._lib import KvqCacheDesc, KvqWindowDesc, check, load
 
 HEAD_DIM = 128
 PAGE_TOKENS = 64
@@ -158,4 +159,107 @@ def kvq_dequant(cache: KVCache, which: int, slots: torch.Tensor, out: torch.Tens
     _dev(out, "out", torch.float32)
     d = cache.desc()
     check(load().kvq_dequant(C.byref(d), which, _ptr(slots), n, _ptr(out), _stream(stream)))
+    return out
+
+
+# --------------------------------------------------------------------------------------
+# Full-precision cache windows ("WUSH-KV" §4.4)
+# --------------------------------------------------------------------------------------
+
+class Window:
+    """Full-precision window rows of one layer: k_win, v_win [num_rows, sink+keep+flush,
+    kv_heads, 128] of `dtype` (the dtype of every activation passed with them)."""
+
+    def __init__(self, cache: KVCache, num_rows: int, sink: int, keep: int, flush: int,
+                 dtype=torch.bfloat16, device="cuda", k_win=None, v_win=None):
+        self.sink, self.keep, self.flush, self.num_rows, self.dtype = sink, keep, flush, num_rows, dtype
+        shape = (num_rows, sink + keep + flush, cache.num_kv_heads, HEAD_DIM)
+        self.k_win = torch.zeros(shape, dtype=dtype, device=device) if k_win is None else k_win
+        self.v_win = torch.zeros(shape, dtype=dtype, device=device) if v_win is None else v_win
+        assert tuple(self.k_win.shape) == shape and tuple(self.v_win.shape) == shape
+        _dev(self.k_win, "k_win", dtype)
+        _dev(self.v_win, "v_win", dtype)
+
+    def desc(self) -> KvqWindowDesc:
+        return KvqWindowDesc(self.sink, self.keep, self.flush, self.num_rows, _DTYPES[self.dtype],
+                             self.k_win.data_ptr(), self.v_win.data_ptr())
+
+
+def kvq_window_prefill(cache: KVCache, win: Window, k: torch.Tensor, v: torch.Tensor,
+                       cu_seqlens: torch.Tensor, block_table: torch.Tensor,
+                       win_rows: torch.Tensor | None = None, t_k: torch.Tensor | None = None,
+                       stream=None) -> None:
+    """Fresh prompts packed as k, v [n, kv_heads, 128] with offsets cu_seqlens [B+1] int32."""
+    _dev(k, "k", win.dtype); _dev(v, "v", win.dtype); _dev(cu_seqlens, "cu_seqlens", torch.int32)
+    _dev(block_table, "block_table", torch.int32); _dev(win_rows, "win_rows", torch.int32)
+    _dev(t_k, "t_k", win.dtype)
+    n = k.shape[0]
+    assert k.shape == (n, cache.num_kv_heads, HEAD_DIM) and v.shape == k.shape
+    B = cu_seqlens.shape[0] - 1
+    d, w = cache.desc(), win.desc()
+    check(load().kvq_window_prefill(C.byref(d), C.byref(w), _ptr(k), _ptr(v), B, _ptr(cu_seqlens), n,
+                                    _ptr(block_table), block_table.shape[1], _ptr(win_rows), _ptr(t_k),
+                                    _stream(stream)))
+
+
+def window_workspace_bytes(cache: KVCache, win: Window, batch: int, num_q_heads: int, max_seq_len: int) -> int:
+    d, w = cache.desc(), win.desc()
+    return int(load().kvq_window_workspace_bytes(C.byref(d), C.byref(w), batch, num_q_heads, max_seq_len))
+
+
+def _window_out_ws(cache, win, q, max_seq_len, out, workspace):
+    B, Hq, _ = q.shape
+    if out is None:
+        out = torch.empty((B, Hq, HEAD_DIM), dtype=torch.float32, device=q.device)
+    _dev(out, "out", torch.float32)
+    need = window_workspace_bytes(cache, win, B, Hq, max_seq_len)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    return out, workspace, ws_bytes
+
+
+def kvq_window_decode_attn(cache: KVCache, win: Window, q: torch.Tensor, block_table: torch.Tensor,
+                           seq_lens: torch.Tensor, max_seq_len: int, win_rows: torch.Tensor | None = None,
+                           t_k_inv_t: torch.Tensor | None = None, sm_scale: float | None = None,
+                           out: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
+                           stream=None) -> torch.Tensor:
+    """Attention over a windowed cache (state after every waiting batch was quantized)."""
+    _dev(q, "q", win.dtype); _dev(block_table, "block_table", torch.int32)
+    _dev(seq_lens, "seq_lens", torch.int32); _dev(win_rows, "win_rows", torch.int32)
+    _dev(t_k_inv_t, "t_k_inv_t", torch.float32)
+    B, Hq, _ = q.shape
+    out, workspace, ws_bytes = _window_out_ws(cache, win, q, max_seq_len, out, workspace)
+    if sm_scale is None:
+        sm_scale = 1.0 / math.sqrt(HEAD_DIM)
+    d, w = cache.desc(), win.desc()
+    check(load().kvq_window_decode_attn(C.byref(d), C.byref(w), _ptr(q), B, Hq, _ptr(t_k_inv_t),
+                                        _ptr(block_table), block_table.shape[1], _ptr(seq_lens),
+                                        _ptr(win_rows), max_seq_len, float(sm_scale), _ptr(out),
+                                        _ptr(workspace), ws_bytes, _stream(stream)))
+    return out
+
+
+def kvq_window_decode_step(cache: KVCache, win: Window, q: torch.Tensor, k_new: torch.Tensor,
+                           v_new: torch.Tensor, block_table: torch.Tensor, seq_lens: torch.Tensor,
+                           max_seq_len: int, win_rows: torch.Tensor | None = None,
+                           t_k: torch.Tensor | None = None, t_k_inv_t: torch.Tensor | None = None,
+                           sm_scale: float | None = None, out: torch.Tensor | None = None,
+                           workspace: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """One decode step: seq_lens [B] counts the new position, whose key and value are
+    k_new, v_new [B, kv_heads, 128]; attention, then the flush of the batch it made eligible."""
+    _dev(q, "q", win.dtype); _dev(k_new, "k_new", win.dtype); _dev(v_new, "v_new", win.dtype)
+    _dev(block_table, "block_table", torch.int32); _dev(seq_lens, "seq_lens", torch.int32)
+    _dev(win_rows, "win_rows", torch.int32); _dev(t_k, "t_k", win.dtype)
+    _dev(t_k_inv_t, "t_k_inv_t", torch.float32)
+    B, Hq, _ = q.shape
+    assert k_new.shape == (B, cache.num_kv_heads, HEAD_DIM) and v_new.shape == k_new.shape
+    out, workspace, ws_bytes = _window_out_ws(cache, win, q, max_seq_len, out, workspace)
+    if sm_scale is None:
+        sm_scale = 1.0 / math.sqrt(HEAD_DIM)
+    d, w = cache.desc(), win.desc()
+    check(load().kvq_window_decode_step(C.byref(d), C.byref(w), _ptr(q), _ptr(k_new), _ptr(v_new), B, Hq,
+                                        _ptr(t_k), _ptr(t_k_inv_t), _ptr(block_table), block_table.shape[1],
+                                        _ptr(seq_lens), _ptr(win_rows), max_seq_len, float(sm_scale),
+                                        _ptr(out), _ptr(workspace), ws_bytes, _stream(stream)))
     return out

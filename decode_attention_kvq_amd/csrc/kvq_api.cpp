@@ -70,9 +70,9 @@ struct WorkspaceLayout {
   size_t o_bytes, ml_bytes, total;
 };
 
-WorkspaceLayout workspace_layout(int batch, int heads_q, int chunks) {
+WorkspaceLayout workspace_layout(int batch, int heads_q, int chunks, bool always = false) {
   WorkspaceLayout w{0, 0, 0};
-  if (batch <= 0 || chunks <= 1) return w;
+  if (batch <= 0 || chunks < 1 || (chunks == 1 && !always)) return w;
   const size_t rows = (size_t)batch * heads_q * chunks;
   w.o_bytes = (rows * 128 * sizeof(float) + 255) & ~(size_t)255;
   w.ml_bytes = (rows * 2 * sizeof(float) + 255) & ~(size_t)255;
@@ -95,11 +95,18 @@ kvq::AppendParams append_params(const kvq_cache_desc* cache, const void* k, cons
   return p;
 }
 
-// Checks and fills the decode launch; shared by kvq_decode_attn and kvq_decode_step.
+// Longest quantized run the decode split is sized for (windows: the sink is never quantized).
+int split_length(int max_seq_len, const kvq::WindowShape* win) {
+  return win ? (max_seq_len > win->sink ? max_seq_len - win->sink : 0) : max_seq_len;
+}
+
+// Checks and fills the decode launch; shared by the plain and windowed decodes.  With
+// windows (win non-null) the partial results always go to the workspace.
 kvq_status decode_params(const kvq_cache_desc* cache, const void* q, kvq_dtype q_dtype, int32_t batch,
                          int32_t num_q_heads, const float* t_k_inv_t, const int32_t* block_table,
                          int32_t max_pages, const int32_t* seq_lens, int32_t max_seq_len, float sm_scale,
-                         float* out, void* workspace, size_t workspace_bytes, kvq::DecodeParams* pp) {
+                         float* out, void* workspace, size_t workspace_bytes, kvq::DecodeParams* pp,
+                         const kvq::WindowShape* win = nullptr) {
   if (batch < 0) return fail(KVQ_ERR_INVALID_ARG, "batch must be >= 0");
   kvq_status s = check_cache(cache, batch > 0, batch > 0);
   if (s != KVQ_OK) return s;
@@ -109,17 +116,19 @@ kvq_status decode_params(const kvq_cache_desc* cache, const void* q, kvq_dtype q
   if (group > 16) return fail(KVQ_ERR_UNSUPPORTED, "at most 16 query heads per KV head");
   if (!valid_dtype(q_dtype)) return fail(KVQ_ERR_INVALID_ARG, "unknown query dtype");
   if (max_seq_len < 0 || max_pages < 0) return fail(KVQ_ERR_INVALID_ARG, "max_seq_len and max_pages must be >= 0");
-  if ((int64_t)max_pages * 64 < (int64_t)max_seq_len)
-    return fail(KVQ_ERR_INVALID_ARG, "max_pages*64 must cover max_seq_len");
+  if ((int64_t)max_pages * 64 < (int64_t)split_length(max_seq_len, win))
+    return fail(KVQ_ERR_INVALID_ARG, win ? "max_pages*64 must cover max_seq_len - sink"
+                                         : "max_pages*64 must cover max_seq_len");
   if (!std::isfinite(sm_scale)) return fail(KVQ_ERR_INVALID_ARG, "sm_scale must be finite");
   if (batch == 0) return KVQ_OK;
   if (batch > 65535) return fail(KVQ_ERR_UNSUPPORTED, "batch must be <= 65535");
   if (!q || !block_table || !seq_lens || !out)
     return fail(KVQ_ERR_INVALID_ARG, "q, block_table, seq_lens and out must be non-null");
-  const kvq::DecodeSplit sp = kvq::decode_split(batch, cache->num_kv_heads, max_seq_len);
-  const WorkspaceLayout wl = workspace_layout(batch, num_q_heads, sp.chunks);
+  const kvq::DecodeSplit sp = kvq::decode_split(batch, cache->num_kv_heads, split_length(max_seq_len, win));
+  const WorkspaceLayout wl = workspace_layout(batch, num_q_heads, sp.chunks, win != nullptr);
   if (wl.total > 0 && (!workspace || workspace_bytes < wl.total))
-    return fail(KVQ_ERR_WORKSPACE, "workspace smaller than kvq_decode_workspace_bytes()");
+    return fail(KVQ_ERR_WORKSPACE, win ? "workspace smaller than kvq_window_workspace_bytes()"
+                                       : "workspace smaller than kvq_decode_workspace_bytes()");
   if (cache->num_pages < 1) return fail(KVQ_ERR_INVALID_ARG, "num_pages must be >= 1");
   kvq::DecodeParams& p = *pp;
   p = kvq::DecodeParams{};
@@ -133,6 +142,26 @@ kvq_status decode_params(const kvq_cache_desc* cache, const void* q, kvq_dtype q
   p.gpad = kvq::decode_group_pad(group);
   p.max_pages = max_pages; p.num_pages = cache->num_pages; p.pages_per_wave = sp.pages_per_wave; p.chunks = sp.chunks;
   p.score_scale = sm_scale * 1.4426950408889634f;
+  if (win) p.win = *win;
+  return KVQ_OK;
+}
+
+size_t elem_bytes(kvq_dtype d) { return d == KVQ_F32 ? 4 : 2; }
+
+// Checks a window descriptor; fills the shape.
+kvq_status check_window(const kvq_cache_desc* cache, const kvq_window_desc* w, bool need_data,
+                        kvq::WindowShape* shape) {
+  if (!w) return fail(KVQ_ERR_INVALID_ARG, "window descriptor is null");
+  if (w->sink < 0 || w->keep < 0 || w->flush < 1)
+    return fail(KVQ_ERR_INVALID_ARG, "window sizes must satisfy sink >= 0, keep >= 0, flush >= 1");
+  if ((int64_t)w->sink + w->keep + w->flush > KVQ_WINDOW_MAX_SLOTS)
+    return fail(KVQ_ERR_UNSUPPORTED, "sink + keep + flush exceeds KVQ_WINDOW_MAX_SLOTS");
+  if (!valid_dtype(w->dtype)) return fail(KVQ_ERR_INVALID_ARG, "unknown window dtype");
+  if (w->num_rows < 0) return fail(KVQ_ERR_INVALID_ARG, "num_rows must be >= 0");
+  if (need_data && (w->num_rows < 1 || !w->k_win || !w->v_win))
+    return fail(KVQ_ERR_INVALID_ARG, "window tensors must be non-null with num_rows >= 1");
+  (void)cache;
+  *shape = kvq::WindowShape{w->sink, w->keep, w->flush};
   return KVQ_OK;
 }
 
@@ -239,6 +268,113 @@ kvq_status kvq_dequant(const kvq_cache_desc* cache, int32_t which, const int64_t
   p.bits = which == 0 ? cache->bits_k : cache->bits_v;
   p.which = which;
   return hip_status(kvq::launch_dequant(p, static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"
+
+extern "C" {
+
+size_t kvq_window_bytes(const kvq_cache_desc* cache, const kvq_window_desc* win) {
+  if (!cache || !win || cache->num_kv_heads < 1 || win->num_rows < 0 || win->sink < 0 || win->keep < 0 ||
+      win->flush < 1 || !valid_dtype(win->dtype))
+    return 0;
+  return (size_t)win->num_rows * (size_t)(win->sink + win->keep + win->flush) * (size_t)cache->num_kv_heads * 128 *
+         elem_bytes(win->dtype);
+}
+
+kvq_status kvq_window_prefill(const kvq_cache_desc* cache, const kvq_window_desc* win, const void* k, const void* v,
+                              int32_t batch, const int32_t* cu_seqlens, int64_t n_tokens,
+                              const int32_t* block_table, int32_t max_pages, const int32_t* win_rows,
+                              const void* t_k, void* stream) {
+  g_last_error.clear();
+  if (batch < 0 || n_tokens < 0 || max_pages < 0)
+    return fail(KVQ_ERR_INVALID_ARG, "batch, n_tokens and max_pages must be >= 0");
+  kvq::WindowShape shape;
+  kvq_status s = check_window(cache, win, batch > 0 && n_tokens > 0, &shape);
+  if (s != KVQ_OK) return s;
+  if ((s = check_cache(cache, n_tokens > 0, n_tokens > 0)) != KVQ_OK) return s;
+  if ((s = check_quantizer(cache->quant_k, cache->alpha_k, cache->p_lo, cache->p_hi)) != KVQ_OK) return s;
+  if ((s = check_quantizer(cache->quant_v, cache->alpha_v, cache->p_lo, cache->p_hi)) != KVQ_OK) return s;
+  if (batch == 0 || n_tokens == 0) return KVQ_OK;
+  if (batch > 65535) return fail(KVQ_ERR_UNSUPPORTED, "batch must be <= 65535");
+  if (n_tokens > 0x7FFFFFFFLL) return fail(KVQ_ERR_UNSUPPORTED, "n_tokens must fit in int32");
+  if (!k || !v || !cu_seqlens || !block_table)
+    return fail(KVQ_ERR_INVALID_ARG, "k, v, cu_seqlens and block_table must be non-null");
+  if (max_pages < 1) return fail(KVQ_ERR_INVALID_ARG, "max_pages must be >= 1");
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  kvq::WindowStoreParams ws{};
+  ws.k = k; ws.v = v; ws.kwin = win->k_win; ws.vwin = win->v_win; ws.cu_seqlens = cu_seqlens;
+  ws.win_rows = win_rows; ws.n = n_tokens; ws.rows = win->num_rows; ws.batch = batch;
+  ws.heads = cache->num_kv_heads; ws.win = shape;
+  if ((s = hip_status(kvq::launch_window_store(ws, (int)win->dtype, st))) != KVQ_OK) return s;
+  kvq::AppendParams a = append_params(cache, k, v, nullptr, n_tokens, t_k);
+  a.slot_mode = kvq::kSlotsPrefill;
+  a.win = shape; a.cu_seqlens = cu_seqlens; a.block_table = block_table; a.win_rows = win_rows;
+  a.batch = batch; a.max_pages = max_pages; a.num_rows = win->num_rows;
+  return hip_status(kvq::launch_append(a, (int)win->dtype, st));
+}
+
+size_t kvq_window_workspace_bytes(const kvq_cache_desc* cache, const kvq_window_desc* win, int32_t batch,
+                                  int32_t num_q_heads, int32_t max_seq_len) {
+  if (!cache || !win || cache->num_kv_heads < 1 || batch <= 0 || num_q_heads < 1 || max_seq_len < 0 ||
+      win->sink < 0)
+    return 0;
+  const kvq::WindowShape shape{win->sink, win->keep, win->flush};
+  const kvq::DecodeSplit sp = kvq::decode_split(batch, cache->num_kv_heads, split_length(max_seq_len, &shape));
+  return workspace_layout(batch, num_q_heads, sp.chunks, true).total;
+}
+
+kvq_status kvq_window_decode_attn(const kvq_cache_desc* cache, const kvq_window_desc* win, const void* q,
+                                  int32_t batch, int32_t num_q_heads, const float* t_k_inv_t,
+                                  const int32_t* block_table, int32_t max_pages, const int32_t* seq_lens,
+                                  const int32_t* win_rows, int32_t max_seq_len, float sm_scale, float* out,
+                                  void* workspace, size_t workspace_bytes, void* stream) {
+  g_last_error.clear();
+  kvq::WindowShape shape;
+  kvq_status s = check_window(cache, win, batch > 0, &shape);
+  if (s != KVQ_OK) return s;
+  kvq::DecodeParams p;
+  s = decode_params(cache, q, win->dtype, batch, num_q_heads, t_k_inv_t, block_table, max_pages, seq_lens,
+                    max_seq_len, sm_scale, out, workspace, workspace_bytes, &p, &shape);
+  if (s != KVQ_OK || batch == 0) return s;
+  p.win_pending = 0;
+  kvq::WindowParams w{win->k_win, win->v_win, win_rows, win->num_rows, nullptr, nullptr};
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  if ((s = hip_status(kvq::launch_decode(p, cache->bits_k, cache->bits_v, (int)win->dtype, st))) != KVQ_OK) return s;
+  return hip_status(kvq::launch_window(p, w, (int)win->dtype, st));
+}
+
+kvq_status kvq_window_decode_step(const kvq_cache_desc* cache, const kvq_window_desc* win, const void* q,
+                                  const void* k_new, const void* v_new, int32_t batch, int32_t num_q_heads,
+                                  const void* t_k, const float* t_k_inv_t, const int32_t* block_table,
+                                  int32_t max_pages, const int32_t* seq_lens, const int32_t* win_rows,
+                                  int32_t max_seq_len, float sm_scale, float* out, void* workspace,
+                                  size_t workspace_bytes, void* stream) {
+  g_last_error.clear();
+  kvq::WindowShape shape;
+  kvq_status s = check_window(cache, win, batch > 0, &shape);
+  if (s != KVQ_OK) return s;
+  kvq::DecodeParams p;
+  s = decode_params(cache, q, win->dtype, batch, num_q_heads, t_k_inv_t, block_table, max_pages, seq_lens,
+                    max_seq_len, sm_scale, out, workspace, workspace_bytes, &p, &shape);
+  if (s != KVQ_OK) return s;
+  if ((s = check_quantizer(cache->quant_k, cache->alpha_k, cache->p_lo, cache->p_hi)) != KVQ_OK) return s;
+  if ((s = check_quantizer(cache->quant_v, cache->alpha_v, cache->p_lo, cache->p_hi)) != KVQ_OK) return s;
+  if (batch == 0) return KVQ_OK;
+  if (!k_new || !v_new) return fail(KVQ_ERR_INVALID_ARG, "k_new and v_new must be non-null");
+  if ((int64_t)batch * shape.flush > 0x7FFFFFFFLL) return fail(KVQ_ERR_UNSUPPORTED, "batch * flush too large");
+  // stream order: the quantized partials, the window (which stores the new position and
+  // merges), then the batches the new positions made eligible are quantized
+  p.win_pending = 1;
+  kvq::WindowParams w{win->k_win, win->v_win, win_rows, win->num_rows, k_new, v_new};
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  if ((s = hip_status(kvq::launch_decode(p, cache->bits_k, cache->bits_v, (int)win->dtype, st))) != KVQ_OK) return s;
+  if ((s = hip_status(kvq::launch_window(p, w, (int)win->dtype, st))) != KVQ_OK) return s;
+  kvq::AppendParams a = append_params(cache, win->k_win, win->v_win, nullptr, (int64_t)batch * shape.flush, t_k);
+  a.slot_mode = kvq::kSlotsFlush;
+  a.win = shape; a.seq_lens = seq_lens; a.block_table = block_table; a.win_rows = win_rows;
+  a.batch = batch; a.max_pages = max_pages; a.num_rows = win->num_rows;
+  return hip_status(kvq::launch_append(a, (int)win->dtype, st));
 }
 
 }  // extern "C"

@@ -323,7 +323,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void a
   const int64_t i = tile0 + tl;
   const bool in_range = i < p.n;
   const int64_t i_ld = in_range ? i : p.n - 1;
-  const int64_t slot = in_range ? p.slots[i] : -1;
+  const int64_t slot = in_range ? token_ref(p, i).slot : -1;   // source row i (given slots, prefill)
   const bool valid = slot >= 0 && slot < p.num_pages * kPageTokens;   // others are skipped
   const int64_t page = valid ? slot / kPageTokens : 0;
   const int o = valid ? (int)(slot % kPageTokens) : 0;
@@ -498,7 +498,7 @@ __global__ __launch_bounds__(64 * kSmallWaves) void append_small_kernel(AppendPa
 template <typename TIn>
 hipError_t launch_typed(const AppendParams& p, hipStream_t stream) {
   const int ksel = select_width(p);
-  if (p.n <= kSmallMaxTokens) {
+  if (p.n <= kSmallMaxTokens || p.slot_mode == kSlotsFlush) {   // a flush reads window rows: small path only
     const dim3 grid((unsigned)p.n, (unsigned)p.heads), block(64 * kSmallWaves);
     if (ksel == 3) hipLaunchKernelGGL((append_small_kernel<TIn, 3>), grid, block, 0, stream, p);
     else hipLaunchKernelGGL((append_small_kernel<TIn, 0>), grid, block, 0, stream, p);

@@ -262,7 +262,10 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
   __shared__ float hconst[GP * 2];
 
   // ---- this wave's pages ----
-  const int nseq = min(p.seq_lens[b], p.max_pages * kPageTokens);
+  // with full-precision windows the cache holds the quantized middle positions only
+  const int nseq = min(p.win.flush > 0 ? window_quantized(max(p.seq_lens[b] - p.win_pending, 0), p.win)
+                                       : p.seq_lens[b],
+                       p.max_pages * kPageTokens);
   const int npages = (nseq + kPageTokens - 1) / kPageTokens;
   const int wv = chunk * kWaves + wave;
   const int pg0 = wv * p.pages_per_wave;
@@ -732,7 +735,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
         }
     }
     const int hq = hq0 + gg;
-    if (p.chunks == 1) {
+    if (p.chunks == 1 && p.win.flush == 0) {
       p.out[((int64_t)b * p.heads_q + hq) * kHeadDim + ch] = L > 0.0f ? O / L : 0.0f;
     } else {
       const int64_t slot = ((int64_t)b * p.heads_q + hq) * p.chunks + chunk;
@@ -774,7 +777,7 @@ hipError_t launch_typed(const DecodeParams& p, hipStream_t stream) {
     default: hipLaunchKernelGGL((decode_kernel<TQ, BK, BV, 16>), grid, dim3(kThreads), 0, stream, p); break;
   }
   hipError_t err = hipGetLastError();
-  if (err != hipSuccess || p.chunks == 1) return err;
+  if (err != hipSuccess || p.chunks == 1 || p.win.flush > 0) return err;   // windows: merged by the window kernel
   hipLaunchKernelGGL(combine_kernel, dim3((unsigned)(p.batch * p.heads_q)), dim3(kHeadDim), 0, stream, p);
   return hipGetLastError();
 }

@@ -1,5 +1,5 @@
-// Per-group encoding shared by the write path and the fused decode step: clip bounds,
-// fp16 scale and zero, codes, and the one-token-per-workgroup append.
+// Per-group encoding of the write path: clip bounds, fp16 scale and zero, codes, the
+// one-token-per-workgroup append, and where a token goes (slot modes).
 //
 // Method: "WUSH-KV: KV Cache Quantization with Data-Adaptive Transforms" §4.2 (key
 // transform after RoPE), §4.3 (RMS clip of a token's 128-channel group), §5.3
@@ -244,7 +244,44 @@ __device__ __forceinline__ void small_quantize_store(float a, float b, bool is_v
   }
 }
 
-// The append of token i (rows of p.k / p.v) for KV head h by one workgroup: waves 0-3 each
+// Cache slot (negative: skip the token) and source row (of p.k / p.v) of token i.
+struct TokenRef {
+  int64_t slot, src;
+};
+__device__ __forceinline__ int64_t window_cache_slot(const AppendParams& p, int64_t b, int64_t j) {
+  if (j < 0 || j / kPageTokens >= p.max_pages) return -1;
+  const int32_t pid = p.block_table[b * p.max_pages + j / kPageTokens];
+  return pid < 0 ? -1 : (int64_t)pid * kPageTokens + j % kPageTokens;
+}
+__device__ __forceinline__ TokenRef token_ref(const AppendParams& p, int64_t i) {
+  if (p.slot_mode == kSlotsGiven) return {p.slots[i], i};
+  if (p.slot_mode == kSlotsPrefill) {
+    // sequence b with cu_seqlens[b] <= i < cu_seqlens[b + 1]; the middle positions
+    // [sink, sink + quantized) of a fresh prompt go to cache index position - sink
+    int lo = 0, hi = p.batch;
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (p.cu_seqlens[mid] <= i) lo = mid;
+      else hi = mid;
+    }
+    const int64_t pos = i - p.cu_seqlens[lo];
+    const int nq = window_quantized(p.cu_seqlens[lo + 1] - p.cu_seqlens[lo], p.win);
+    if (pos < p.win.sink || pos >= p.win.sink + nq) return {-1, i};
+    return {window_cache_slot(p, lo, pos - p.win.sink), i};
+  }
+  // flush after a decode step: sequence b quantizes the batch that its new position made
+  // eligible (if any), reading the window row's ring slots
+  const int64_t b = i / p.win.flush;
+  const int f = (int)(i % p.win.flush);
+  const int len = max(p.seq_lens[b], 0);
+  const int q0 = window_quantized(max(len - 1, 0), p.win), q1 = window_quantized(len, p.win);
+  const int row = p.win_rows ? p.win_rows[b] : (int)b;
+  if (f >= q1 - q0 || row < 0 || row >= p.num_rows) return {-1, 0};
+  const int j = q0 + f;
+  return {window_cache_slot(p, b, j), (int64_t)row * window_width(p.win) + window_slot(p.win.sink + j, p.win)};
+}
+
+// The append of token i (its row of p.k / p.v from token_ref) for KV head h by one workgroup: waves 0-3 each
 // multiply a quarter of the rows of T (all their loads in flight at once), wave 0 adds the
 // four partial products in order and writes the key, wave VW writes the value (before the
 // workgroup barrier when VW >= 4, after it otherwise).  Every wave of the workgroup must
@@ -252,12 +289,13 @@ __device__ __forceinline__ void small_quantize_store(float a, float b, bool is_v
 template <typename TIn, int KSEL, int VW>
 __device__ __forceinline__ void append_token(const AppendParams& p, int64_t i, int h, int wave, int lane,
                                              float (*part)[kHeadDim]) {
-  const int64_t slot = p.slots[i];
+  const TokenRef ref = token_ref(p, i);
+  const int64_t slot = ref.slot;
   if (slot < 0 || slot >= p.num_pages * kPageTokens) return;   // skipped (whole workgroup)
   const int64_t page = slot / kPageTokens;
   const int o = (int)(slot % kPageTokens);
-  const TIn* krow = reinterpret_cast<const TIn*>(p.k) + (i * p.heads + h) * kHeadDim;
-  const TIn* vrow = reinterpret_cast<const TIn*>(p.v) + (i * p.heads + h) * kHeadDim;
+  const TIn* krow = reinterpret_cast<const TIn*>(p.k) + (ref.src * p.heads + h) * kHeadDim;
+  const TIn* vrow = reinterpret_cast<const TIn*>(p.v) + (ref.src * p.heads + h) * kHeadDim;
   if (VW >= 4 && wave == VW) {
     const float2 v = load_pair<TIn>(vrow, lane);
     small_quantize_store<KSEL>(v.x, v.y, true, page, o, h, lane, p);

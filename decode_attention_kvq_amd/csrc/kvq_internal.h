@@ -6,6 +6,36 @@
 
 namespace kvq {
 
+// Full-precision cache windows: positions [0, sink) and the newest positions of a sequence
+// stay in full precision; a position from `sink` on is eligible once `keep` newer ones
+// exist, and eligible positions are quantized in batches of `flush`, oldest first, as soon
+// as `flush` of them wait.  The paged cache holds quantized position p at index p - sink.
+// The full-precision positions live in a window row of sink + keep + flush slots: the sink
+// at slots [0, sink), every later position p in the ring slot sink + (p - sink) % (keep + flush).
+struct WindowShape {
+  int sink, keep, flush;   // flush == 0: no window
+};
+
+// Quantized positions of a sequence of `len` positions once every waiting batch has been
+// quantized (positions sink .. sink + result - 1).
+__host__ __device__ inline int window_quantized(int len, const WindowShape& w) {
+  const int e = len - w.sink - w.keep;
+  return e >= w.flush ? e / w.flush * w.flush : 0;
+}
+__host__ __device__ inline int window_slot(int pos, const WindowShape& w) {
+  return pos < w.sink ? pos : w.sink + (pos - w.sink) % (w.keep + w.flush);
+}
+__host__ __device__ inline int window_width(const WindowShape& w) { return w.sink + w.keep + w.flush; }
+
+// Where the append kernels find a token's cache slot and source row.
+enum SlotMode {
+  kSlotsGiven = 0,      // slot = slots[i], source row i of k / v
+  kSlotsPrefill = 1,    // windowed prefill: token i is position i - cu_seqlens[b] of sequence b
+                        // (source row i); middle positions go to index position - sink
+  kSlotsFlush = 2,      // window flush of a decode step: token i is batch entry i % flush of
+                        // sequence i / flush; source rows are window slots (k / v = the windows)
+};
+
 struct AppendParams {
   const void* k;
   const void* v;
@@ -21,6 +51,14 @@ struct AppendParams {
   int ilo, ihi;           // percentile order-statistic positions (0..127)
   float flo, fhi;         // interpolation weights
   float alpha_k, alpha_v;
+  // slot modes other than kSlotsGiven
+  int slot_mode;
+  WindowShape win;
+  const int32_t* cu_seqlens;   // [batch + 1] (prefill)
+  const int32_t* seq_lens;     // [batch] (flush: lengths after the step)
+  const int32_t* block_table;  // [batch][max_pages]
+  const int32_t* win_rows;     // [batch] window row of each sequence, or null (row b)
+  int batch, max_pages, num_rows;
 };
 
 // Width of the insertion networks that hold every order statistic the percentile clip
@@ -54,6 +92,36 @@ struct DecodeParams {
   int pages_per_wave;
   int chunks;             // workgroups per (sequence, KV head)
   float score_scale;      // sm_scale * log2(e)
+  // full-precision windows (win.flush == 0: none): the cache holds the quantized middle
+  // positions only, window_quantized(seq_len - win_pending) of them; the partial results
+  // always go to the workspace, and the window kernel merges them
+  WindowShape win;
+  int win_pending;
+};
+
+// The window half of a windowed decode: attention over the full-precision positions, the
+// merge with the quantized partials, and (decode step) the store of the new token.
+struct WindowParams {
+  void* kwin;             // [rows][sink + keep + flush][Hkv][128] of the query dtype
+  void* vwin;
+  const int32_t* win_rows;
+  int rows;
+  const void* k_new;      // [B][Hkv][128] or null: the step's new token (position seq_len - 1)
+  const void* v_new;
+};
+
+// Prefill of the windows: copies the full-precision positions of each sequence from the
+// packed prompt rows into its window row.
+struct WindowStoreParams {
+  const void* k;
+  const void* v;
+  void* kwin;
+  void* vwin;
+  const int32_t* cu_seqlens;
+  const int32_t* win_rows;
+  int64_t n;              // packed prompt rows
+  int rows, batch, heads;
+  WindowShape win;
 };
 
 struct DequantParams {
@@ -72,6 +140,8 @@ hipError_t launch_append(const AppendParams& p, int in_dtype, hipStream_t stream
 hipError_t launch_decode(const DecodeParams& p, int bits_k, int bits_v, int q_dtype,
                          hipStream_t stream);
 hipError_t launch_dequant(const DequantParams& p, hipStream_t stream);
+hipError_t launch_window(const DecodeParams& p, const WindowParams& w, int q_dtype, hipStream_t stream);
+hipError_t launch_window_store(const WindowStoreParams& p, int dtype, hipStream_t stream);
 
 // Split of a decode launch, a function of the shapes only.
 struct DecodeSplit {

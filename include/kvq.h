@@ -176,6 +176,96 @@ kvq_status kvq_decode_step(const kvq_cache_desc* cache, const void* q, const voi
 kvq_status kvq_dequant(const kvq_cache_desc* cache, int32_t which, const int64_t* slots,
                        int64_t n_tokens, float* out, void* stream);
 
+/* ---------------------------------------------------------------------------------
+ * Full-precision cache windows ("WUSH-KV: KV Cache Quantization with Data-Adaptive
+ * Transforms" §4.4; §4.5 for their size).  The first `sink` positions and the newest
+ * positions of a sequence stay in full precision.  A position p >= sink is eligible once
+ * `keep` newer positions exist; eligible positions are quantized, oldest first, in batches
+ * of `flush` as soon as `flush` of them wait.  Hence, once every waiting batch has been
+ * quantized, a sequence of L positions has
+ *     Q(L) = flush * floor((L - sink - keep) / flush)   (0 when L - sink - keep < flush)
+ * quantized positions sink .. sink+Q-1, held in the paged cache at index p - sink
+ * (page block_table[b][(p - sink)/64], offset (p - sink)%64); positions 0 .. sink-1 and
+ * sink+Q .. L-1 are read in full precision.  A decode step reads its new position in full
+ * precision and quantizes the batch it makes eligible after its attention.
+ *
+ * Window tensors (k_win, v_win): device, [num_rows][sink + keep + flush][num_kv_heads][128]
+ * of `dtype`, caller-owned.  Sequence b uses row win_rows[b] (row b when win_rows is NULL;
+ * a row outside [0, num_rows) gives it no full-precision positions and nothing is written
+ * there).  Position p < sink is slot p; a later position p is slot
+ * sink + (p - sink) % (keep + flush).  Keys are stored as given (post-RoPE, before the key
+ * transform), so their scores use the plain query; values in the folded basis as given.
+ * Queries, new keys and values, prompts and T_K are all of `dtype`.
+ * --------------------------------------------------------------------------------- */
+enum { KVQ_WINDOW_MAX_SLOTS = 65535 };   /* largest sink + keep + flush */
+
+typedef struct kvq_window_desc {
+  int32_t sink;           /* S_sink >= 0 */
+  int32_t keep;           /* S_keep >= 0 */
+  int32_t flush;          /* S_flush >= 1 */
+  int32_t num_rows;       /* window rows (sequences in flight) */
+  kvq_dtype dtype;        /* element type of the windows and of every activation passed */
+  void* k_win;            /* device, see above */
+  void* v_win;
+} kvq_window_desc;
+
+/* Bytes of one window tensor (k_win or v_win); 0 for an invalid descriptor. */
+size_t kvq_window_bytes(const kvq_cache_desc* cache, const kvq_window_desc* win);
+
+/* Prefill of fresh prompts into a windowed cache: after the call, prompt b of length
+ * L = cu_seqlens[b+1] - cu_seqlens[b] is in the state above with Q(L) quantized positions
+ * (written exactly as kvq_quantize_append writes them, T_K applied) and its other
+ * positions in window row win_rows[b].
+ *   k, v          device, [n_tokens][num_kv_heads][128] of win->dtype, the prompts packed
+ *                 back to back; cu_seqlens device [batch+1] int32 offsets (cu_seqlens[0] = 0,
+ *                 non-decreasing, cu_seqlens[batch] <= n_tokens).
+ *   block_table   device, [batch][max_pages] int32 (cache index j of sequence b in page
+ *                 block_table[b][j/64]; an index past max_pages pages is not written).
+ *   t_k           device, [num_kv_heads][128][128] of win->dtype, or NULL (identity).
+ * Two kernels in stream order (window store, quantize-append). */
+kvq_status kvq_window_prefill(const kvq_cache_desc* cache, const kvq_window_desc* win,
+                              const void* k, const void* v, int32_t batch,
+                              const int32_t* cu_seqlens, int64_t n_tokens,
+                              const int32_t* block_table, int32_t max_pages,
+                              const int32_t* win_rows, const void* t_k, void* stream);
+
+/* Workspace bytes of kvq_window_decode_attn / kvq_window_decode_step for these sizes
+ * (always non-zero for batch >= 1: the quantized partials are merged with the window). */
+size_t kvq_window_workspace_bytes(const kvq_cache_desc* cache, const kvq_window_desc* win,
+                                  int32_t batch, int32_t num_q_heads, int32_t max_seq_len);
+
+/* Read path over a windowed cache: attention of q over all seq_lens[b] positions, Q(L)
+ * quantized (read as by kvq_decode_attn, with q . T_K^-T) and the rest from the window
+ * with q; one softmax over both.  Arguments as in kvq_decode_attn, q of win->dtype, except
+ * that block_table covers the quantized positions only: max_pages*64 >= max_seq_len - sink.
+ * The state read is the one after every waiting batch was quantized (after a prefill or a
+ * decode step).  Two kernels: quantized partials, then window attention and merge. */
+kvq_status kvq_window_decode_attn(const kvq_cache_desc* cache, const kvq_window_desc* win,
+                                  const void* q, int32_t batch, int32_t num_q_heads,
+                                  const float* t_k_inv_t, const int32_t* block_table,
+                                  int32_t max_pages, const int32_t* seq_lens,
+                                  const int32_t* win_rows, int32_t max_seq_len,
+                                  float sm_scale, float* out, void* workspace,
+                                  size_t workspace_bytes, void* stream);
+
+/* One decode step over a windowed cache.  seq_lens[b] = L counts the new position L-1,
+ * whose key and value are k_new[b], v_new[b] ([batch][num_kv_heads][128] of win->dtype).
+ * In stream order: attention over the state with Q(L-1) quantized positions and the new
+ * position in full precision (the new key and value are stored in the window); then, if
+ * Q(L) > Q(L-1), the batch of positions sink+Q(L-1) .. sink+Q(L)-1 is quantized from the
+ * window into the paged cache (with t_k, as kvq_quantize_append).  Other arguments as in
+ * kvq_window_decode_attn.  Kernels: quantized partials, window attention and merge (which
+ * stores the new position), flush.  The flush launches batch*flush one-token workgroups,
+ * of which those without a batch to quantize return at once. */
+kvq_status kvq_window_decode_step(const kvq_cache_desc* cache, const kvq_window_desc* win,
+                                  const void* q, const void* k_new, const void* v_new,
+                                  int32_t batch, int32_t num_q_heads, const void* t_k,
+                                  const float* t_k_inv_t, const int32_t* block_table,
+                                  int32_t max_pages, const int32_t* seq_lens,
+                                  const int32_t* win_rows, int32_t max_seq_len,
+                                  float sm_scale, float* out, void* workspace,
+                                  size_t workspace_bytes, void* stream);
+
 const char* kvq_status_string(kvq_status status);
 
 /* Message describing the calling thread's last non-OK status ("" if none). */

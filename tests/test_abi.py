@@ -154,3 +154,82 @@ def test_decode_step_argument_checks(lib):
     assert call(d=_desc(p_lo=0.7, p_hi=0.2)) == -1
     assert call(d=_desc(quant_k=1, alpha_k=-1.0)) == -1
     assert call(B=1, mp=256, msl=16384) == -3   # split launch without a workspace
+
+
+def test_window_descriptor_layout_matches_c():
+    src = r"""
+    #include <stddef.h>
+    #include <stdio.h>
+    #include "kvq.h"
+    int main(void) {
+      printf("%zu %zu %zu %zu %zu %d\n", sizeof(kvq_window_desc), offsetof(kvq_window_desc, num_rows),
+             offsetof(kvq_window_desc, dtype), offsetof(kvq_window_desc, k_win),
+             offsetof(kvq_window_desc, v_win), (int)KVQ_WINDOW_MAX_SLOTS);
+      return 0;
+    }"""
+    with tempfile.TemporaryDirectory() as d:
+        c = os.path.join(d, "w.c")
+        exe = os.path.join(d, "w")
+        open(c, "w").write(src)
+        subprocess.check_call(["gcc", "-std=c11", "-I", os.path.join(ROOT, "include"), c, "-o", exe])
+        got = subprocess.check_output([exe]).decode().split()
+    W = _lib.KvqWindowDesc
+    assert [int(x) for x in got] == [C.sizeof(W), W.num_rows.offset, W.dtype.offset, W.k_win.offset,
+                                      W.v_win.offset, 65535]
+
+
+def _win(**kw):
+    w = dict(sink=4, keep=16, flush=16, num_rows=2, dtype=1, k_win=0x3000, v_win=0x4000)
+    w.update(kw)
+    return _lib.KvqWindowDesc(**w)
+
+
+def test_window_sizes(lib):
+    d = _desc()
+    assert lib.kvq_window_bytes(C.byref(d), C.byref(_win())) == 2 * 36 * 8 * 128 * 2
+    assert lib.kvq_window_bytes(C.byref(d), C.byref(_win(dtype=0))) == 2 * 36 * 8 * 128 * 4
+    assert lib.kvq_window_bytes(C.byref(d), C.byref(_win(flush=0))) == 0
+    # windowed decodes always merge through the workspace, even unsplit
+    assert lib.kvq_decode_workspace_bytes(C.byref(d), 64, 32, 256) == 0
+    assert lib.kvq_window_workspace_bytes(C.byref(d), C.byref(_win()), 64, 32, 256) >= 64 * 32 * 130 * 4
+
+
+def test_window_argument_checks(lib):
+    d = _desc()
+    p = C.c_void_p(0x10)
+
+    def attn(**kw):
+        return lib.kvq_window_decode_attn(
+            C.byref(kw.get("d", d)), C.byref(kw.get("w", _win())), kw.get("q", p), kw.get("B", 2),
+            kw.get("Hq", 32), None, kw.get("bt", p), kw.get("mp", 4), kw.get("sl", p), None,
+            kw.get("msl", 256), 0.088, kw.get("out", p), kw.get("ws", p), kw.get("wsb", 0), None)
+
+    def step(**kw):
+        return lib.kvq_window_decode_step(
+            C.byref(kw.get("d", d)), C.byref(kw.get("w", _win())), p, kw.get("k", p), kw.get("v", p),
+            kw.get("B", 2), 32, None, None, p, 4, p, None, 256, 0.088, p, p, kw.get("wsb", 1 << 20), None)
+
+    def prefill(**kw):
+        return lib.kvq_window_prefill(
+            C.byref(kw.get("d", d)), C.byref(kw.get("w", _win())), kw.get("k", p), p, kw.get("B", 2),
+            kw.get("cu", p), kw.get("n", 100), kw.get("bt", p), kw.get("mp", 4), None, None, None)
+
+    assert attn(w=_win(flush=0)) == -1
+    assert attn(w=_win(sink=-1)) == -1
+    assert attn(w=_win(sink=40000, keep=30000)) == -2
+    assert attn(w=_win(dtype=7)) == -1
+    assert attn(w=_win(k_win=None)) == -1
+    assert attn(w=_win(num_rows=0)) == -1
+    assert attn(Hq=30) == -1
+    assert attn(mp=3) == -1
+    assert attn() == -3                          # always needs a workspace
+    assert attn(B=0) == 0
+    assert step(k=None) == -1
+    assert step(d=_desc(p_lo=0.7, p_hi=0.2)) == -1
+    assert step(wsb=0) == -3
+    assert step(B=0) == 0
+    assert prefill(cu=None) == -1
+    assert prefill(mp=0) == -1
+    assert prefill(w=_win(flush=0)) == -1
+    assert prefill(n=0) == 0
+    assert prefill(B=0) == 0
