@@ -119,34 +119,82 @@ def time_steps(w, s, torch, api, steps, warmup):
 
     step()                                   # first call (library load) outside the graphs
     torch.cuda.synchronize()
+    ms_step, wall_step = graph_time(torch, step, steps, warmup)
+    ms_app, _ = graph_time(torch, append, steps, warmup)
+    ms_dec, _ = graph_time(torch, decode, steps, warmup)
+    return dict(step=ms_step, wall=wall_step, append=ms_app, decode=ms_dec)
 
-    def capture(fn, count):
+
+def graph_time(torch, fn, steps, warmup):
+    """ms per call of fn: one replay of a HIP graph of `steps` calls (captured from the
+    library calls on torch's current stream) after one replay of a graph of `warmup`
+    calls, bracketed by HIP events on the launch stream; also the host wall time."""
+
+    def capture(count):
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
             for _ in range(count):
                 fn()
         return g
 
-    def timed(fn):
-        gw, gt = capture(fn, max(warmup, 1)), capture(fn, steps)
-        torch.cuda.synchronize()
-        gw.replay()
-        torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        t0 = time.perf_counter()
-        e0.record()
-        gt.replay()
-        e1.record()
-        torch.cuda.synchronize()
-        ms = e0.elapsed_time(e1) / steps
-        wall = (time.perf_counter() - t0) * 1e3 / steps
-        del gw, gt
-        return ms, wall
+    gw, gt = capture(max(warmup, 1)), capture(steps)
+    torch.cuda.synchronize()
+    gw.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record()
+    gt.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    wall = (time.perf_counter() - t0) * 1e3 / steps
+    del gw, gt
+    return ms, wall
 
-    ms_step, wall_step = timed(step)
-    ms_app, _ = timed(append)
-    ms_dec, _ = timed(decode)
-    return dict(step=ms_step, wall=wall_step, append=ms_app, decode=ms_dec)
+
+WINDOW = (32, 64, 64)          # S_sink, S_keep, S_flush: at most 159 full-precision positions
+
+
+def time_window(w, s, torch, api, steps, warmup):
+    """The decode step over a windowed cache (kvq_window_decode_step) on the workload's
+    cache: full-precision windows of S_sink = 32, S_keep = 64, S_flush = 64 positions (under
+    1% of the 16K context) in bf16.  Timed at a length whose step quantizes nothing (63 of
+    every 64 steps) and at one whose step quantizes a batch of 64 positions in every
+    sequence; the amortised step is (63 x plain + flush) / 64."""
+    sink, keep, flush = WINDOW
+    B, H = w.batch, w.heads_kv
+    dev = s["q"].device
+    win = api.Window(s["cache"], B, sink, keep, flush, dtype=torch.bfloat16, device=dev)
+    g = torch.Generator(device=dev)
+    g.manual_seed(4242)
+    win.k_win.copy_(torch.randn(win.k_win.shape, generator=g, device=dev))
+    win.v_win.copy_(torch.randn(win.v_win.shape, generator=g, device=dev))
+    ws = torch.empty(api.window_workspace_bytes(s["cache"], win, B, w.heads_q, w.seq_len), dtype=torch.uint8,
+                     device=dev)
+    plain_len = w.seq_len                                   # (16384 - 96) % 64 != 0: no batch completes
+    flush_len = sink + keep + flush * ((w.seq_len - sink - keep) // flush)   # a batch completes
+    res = {}
+    for name, L in (("step", plain_len), ("flush_step", flush_len)):
+        lens = torch.full((B,), L, dtype=torch.int32, device=dev)
+
+        def step():
+            api.kvq_window_decode_step(s["cache"], win, s["q"], s["knew"], s["vnew"], s["bt"], lens, w.seq_len,
+                                       t_k=s["t_k"], t_k_inv_t=s["t_inv"], out=s["out"], workspace=ws)
+        step()
+        torch.cuda.synchronize()
+        res[name] = graph_time(torch, step, steps, warmup)[0]
+    lens = torch.full((B,), plain_len, dtype=torch.int32, device=dev)
+
+    def read():
+        api.kvq_window_decode_attn(s["cache"], win, s["q"], s["bt"], lens, w.seq_len, t_k_inv_t=s["t_inv"],
+                                   out=s["out"], workspace=ws)
+    res["read"] = graph_time(torch, read, steps, warmup)[0]
+    amort = (63 * res["step"] + res["flush_step"]) / 64
+    return {"window": {"sink": sink, "keep": keep, "flush": flush, "dtype": "bf16"},
+            "step_us": res["step"] * 1e3, "flush_step_us": res["flush_step"] * 1e3,
+            "amortised_step_us": amort * 1e3, "read_us": res["read"] * 1e3,
+            "tokens_per_s": B * w.seq_len / (amort * 1e-3)}
 
 
 def time_prefill(w, torch, api, calib, synth, dev, reps=20):
@@ -262,10 +310,11 @@ def main():
         "decode_us": t["decode"] * 1e3,
         "decode_tokens_per_s": cached / (t["decode"] * 1e-3),
     }
+    if args.extra:
+        extra = {w.name + "-window": time_window(w, s, torch, api, args.steps, args.warmup)}
     del s
     torch.cuda.empty_cache()
     if args.extra:
-        extra = {}
         for name in ("qwen3-8b-b1-16k", "long-b16-128k-quest"):
             w2 = synth.WORKLOADS[name]
             s2 = setup_decode(w2, torch, api, calib, synth, dev)

@@ -322,12 +322,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void a
   const int64_t tile0 = (int64_t)blockIdx.x * kBlockTokens + wave * kTileTokens;
   const int64_t i = tile0 + tl;
   const bool in_range = i < p.n;
-  const int64_t i_ld = in_range ? i : p.n - 1;
-  const int64_t slot = in_range ? token_ref(p, i).slot : -1;   // source row i (given slots, prefill)
+  const TokenRef ref = in_range ? token_ref(p, i) : TokenRef{-1, 0};   // (row 0 exists)
+  const int64_t slot = ref.slot;
   const bool valid = slot >= 0 && slot < p.num_pages * kPageTokens;   // others are skipped
+  // a window flush's workgroup without a token to write (most of them) ends here; other
+  // batches skip the vote, whose barrier would hold the row loads behind the slot loads
+  if (p.slot_mode == kSlotsFlush && !__syncthreads_or(valid)) return;
   const int64_t page = valid ? slot / kPageTokens : 0;
   const int o = valid ? (int)(slot % kPageTokens) : 0;
-  const TIn* row = reinterpret_cast<const TIn*>(is_v ? p.v : p.k) + (i_ld * p.heads + h) * kHeadDim;
+  const TIn* row = reinterpret_cast<const TIn*>(is_v ? p.v : p.k) + (ref.src * p.heads + h) * kHeadDim;
   constexpr bool kMfmaType = sizeof(TIn) == 2;
 
   float x[64];
@@ -498,7 +501,7 @@ __global__ __launch_bounds__(64 * kSmallWaves) void append_small_kernel(AppendPa
 template <typename TIn>
 hipError_t launch_typed(const AppendParams& p, hipStream_t stream) {
   const int ksel = select_width(p);
-  if (p.n <= kSmallMaxTokens || p.slot_mode == kSlotsFlush) {   // a flush reads window rows: small path only
+  if (p.n <= kSmallMaxTokens) {
     const dim3 grid((unsigned)p.n, (unsigned)p.heads), block(64 * kSmallWaves);
     if (ksel == 3) hipLaunchKernelGGL((append_small_kernel<TIn, 3>), grid, block, 0, stream, p);
     else hipLaunchKernelGGL((append_small_kernel<TIn, 0>), grid, block, 0, stream, p);

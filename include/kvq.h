@@ -255,8 +255,8 @@ kvq_status kvq_window_decode_attn(const kvq_cache_desc* cache, const kvq_window_
  * Q(L) > Q(L-1), the batch of positions sink+Q(L-1) .. sink+Q(L)-1 is quantized from the
  * window into the paged cache (with t_k, as kvq_quantize_append).  Other arguments as in
  * kvq_window_decode_attn.  Kernels: quantized partials, window attention and merge (which
- * stores the new position), flush.  The flush launches batch*flush one-token workgroups,
- * of which those without a batch to quantize return at once. */
+ * stores the new position), flush.  The flush covers batch*flush candidate positions;
+ * workgroups whose positions have nothing to quantize return at once. */
 kvq_status kvq_window_decode_step(const kvq_cache_desc* cache, const kvq_window_desc* win,
                                   const void* q, const void* k_new, const void* v_new,
                                   int32_t batch, int32_t num_q_heads, const void* t_k,

@@ -191,6 +191,9 @@ STEP_CASES = [
     Case(2, 5, 16, [1, 30, 63], (4, 2), "bf16", True, 4, rows_perm=True),
     Case(0, 1, 4, [9, 2], (2, 4), "f32", True, 8, H=1),
     Case(6, 0, 2, [6, 7, 50], (2, 2), "f16", False, 2),
+    # batch x flush > 512 candidate positions: the flush runs on the 128-token tile kernel
+    Case(4, 8, 64, [50, 60, 70, 100, 120, 130, 140, 75, 200], (2, 2), "bf16", False, 4),
+    Case(4, 8, 64, [50, 60, 70, 100, 120, 130, 140, 75, 200], (4, 4), "f16", True, 4, rows_perm=True),
 ]
 
 
