@@ -231,7 +231,8 @@ void oracle_quantize_rows(const float* x, int64_t rows, int bits, int quantizer,
 /*                                                                           */
 /* A pool is [num_pages][kv_heads] blocks.  One block holds 64 tokens of one  */
 /* KV head:                                                                  */
-/*   codes   64*128*bits/8 bytes, read as little-endian 32-bit words          */
+/*   codes   64*128*bits/8 bytes, read as little-endian 32-bit words (2 or 4 */
+/*           bits as below; 3 bits as two planes, see high_plane_position)    */
 /*     keys:   word (o * 128*bits/32 + c/(32/bits)), bit (c % (32/bits))*bits  */
 /*             (token-major rows)                                             */
 /*     values: word ((o/(32/bits)) * 128 + c),      bit (o % (32/bits))*bits   */
@@ -264,6 +265,34 @@ static void code_position(int which, int bits, int o, int c, int64_t* word, int*
     else            { *word = (int64_t)(o / per_word) * HEAD_DIM + c;             *bit = (o % per_word) * bits; }
 }
 
+/* 3-bit codes are kept as two bit planes, so that each plane packs whole words:     */
+/*   low plane  (bits 0-1 of every code): the 2-bit code section, word for word;     */
+/*   high plane (bit 2 of every code): 1024 bytes after the low plane (word 512 on):  */
+/*     keys    token o's 128 bits are words o*4 + c/32; channel offset u = c % 32 is */
+/*             at bit 4*((u % 16)/2) + 2*(u/16) + u % 2                               */
+/*     values  word (o/32)*128 + c holds tokens 32*(o/32) .. +31 of channel c; token */
+/*             offset t = o % 32 is at bit t % 8 + 16*((t/8) % 2) + 8*(t/16)          */
+/* (the in-word orders are a layout choice of this cache; any bijection would do)    */
+static void high_plane_position(int which, int o, int c, int64_t* word, int* bit)
+{
+    const int64_t base = (int64_t)PAGE_TOKENS * HEAD_DIM * 2 / 32;   /* words of the low plane */
+    if (which == 0) {
+        int u = c % 32;
+        *word = base + (int64_t)o * 4 + c / 32;
+        *bit = 4 * ((u % 16) / 2) + 2 * (u / 16) + u % 2;
+    } else {
+        int t = o % 32;
+        *word = base + (int64_t)(o / 32) * HEAD_DIM + c;
+        *bit = t % 8 + 16 * ((t / 8) % 2) + 8 * (t / 16);
+    }
+}
+
+static void put_bits(uint8_t* block, int64_t w, int b, uint32_t mask, uint32_t v)
+{
+    uint32_t word = load_word(block + 4 * w);
+    store_word(block + 4 * w, (word & ~(mask << b)) | ((v & mask) << b));
+}
+
 static uint8_t* block_at(uint8_t* pool, int64_t page, int h, int kv_heads, int bits)
 {
     return pool + (page * kv_heads + h) * oracle_block_bytes(bits);
@@ -274,13 +303,17 @@ static uint8_t* block_at(uint8_t* pool, int64_t page, int h, int kv_heads, int b
 void oracle_pack_token(uint8_t* block, int which, int bits, int o, const uint8_t* codes,
                        uint16_t scale_h, uint16_t zero_h)
 {
-    uint32_t mask = (1u << bits) - 1u;
     for (int c = 0; c < HEAD_DIM; ++c) {
         int64_t w; int b;
-        code_position(which, bits, o, c, &w, &b);
-        uint32_t word = load_word(block + 4 * w);
-        word = (word & ~(mask << b)) | ((uint32_t)codes[c] << b);
-        store_word(block + 4 * w, word);
+        if (bits == 3) {
+            code_position(which, 2, o, c, &w, &b);
+            put_bits(block, w, b, 3u, codes[c]);
+            high_plane_position(which, o, c, &w, &b);
+            put_bits(block, w, b, 1u, (uint32_t)codes[c] >> 2);
+        } else {
+            code_position(which, bits, o, c, &w, &b);
+            put_bits(block, w, b, (1u << bits) - 1u, codes[c]);
+        }
     }
     uint8_t* meta = block + (int64_t)PAGE_TOKENS * HEAD_DIM * bits / 8;
     meta[2 * o] = (uint8_t)(scale_h & 0xFF); meta[2 * o + 1] = (uint8_t)(scale_h >> 8);
@@ -291,11 +324,17 @@ void oracle_pack_token(uint8_t* block, int which, int bits, int o, const uint8_t
 void oracle_unpack_token(const uint8_t* block, int which, int bits, int o, uint8_t* codes,
                          uint16_t* scale_h, uint16_t* zero_h)
 {
-    uint32_t mask = (1u << bits) - 1u;
     for (int c = 0; c < HEAD_DIM; ++c) {
         int64_t w; int b;
-        code_position(which, bits, o, c, &w, &b);
-        codes[c] = (uint8_t)((load_word(block + 4 * w) >> b) & mask);
+        if (bits == 3) {
+            code_position(which, 2, o, c, &w, &b);
+            uint32_t lo = (load_word(block + 4 * w) >> b) & 3u;
+            high_plane_position(which, o, c, &w, &b);
+            codes[c] = (uint8_t)(lo | (((load_word(block + 4 * w) >> b) & 1u) << 2));
+        } else {
+            code_position(which, bits, o, c, &w, &b);
+            codes[c] = (uint8_t)((load_word(block + 4 * w) >> b) & ((1u << bits) - 1u));
+        }
     }
     const uint8_t* meta = block + (int64_t)PAGE_TOKENS * HEAD_DIM * bits / 8;
     *scale_h = (uint16_t)(meta[2 * o] | (meta[2 * o + 1] << 8));

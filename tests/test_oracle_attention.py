@@ -48,9 +48,9 @@ def _sdpa_reference(orc, kp, vp, bt, seq, q, tinv, bits):
     return out
 
 
+@pytest.mark.parametrize("bits", [(2, 4), (3, 3), (3, 2)])
 @pytest.mark.parametrize("t", [False, True])
-def test_matches_torch_sdpa_fp64(orc, t):
-    bits = (2, 4)
+def test_matches_torch_sdpa_fp64(orc, t, bits):
     kp, vp, bt, seq, _, q, tinv = _setup(orc, bits=bits, t=t)
     got = orc.decode_attention(kp, vp, q, bt, seq, t_inv_t=tinv, bits_k=bits[0], bits_v=bits[1])
     ref = _sdpa_reference(orc, kp, vp, bt, seq, q, tinv, bits)

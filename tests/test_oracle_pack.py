@@ -9,7 +9,7 @@ GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "pack_layout.json")
 
 
 def _code_fn(expr):
-    return {"c % 4": lambda c: c % 4, "c % 16": lambda c: c % 16,
+    return {"c % 4": lambda c: c % 4, "c % 8": lambda c: c % 8, "c % 16": lambda c: c % 16,
             "15 - c % 16": lambda c: 15 - c % 16}[expr]
 
 
@@ -42,7 +42,7 @@ def test_golden_words(orc):
         assert nbytes * 8 / (64 * 128) == g["bits_per_element"][bits]
 
 
-@pytest.mark.parametrize("bits", [2, 4])
+@pytest.mark.parametrize("bits", [2, 3, 4])
 @pytest.mark.parametrize("which", [0, 1])
 def test_round_trip_and_isolation(orc, bits, which):
     rng = np.random.default_rng(bits * 10 + which)
@@ -88,3 +88,28 @@ def test_append_skips_negative_and_rejects_out_of_range(orc):
     assert not kp.any() and not vp.any()
     with pytest.raises(ValueError):
         orc.append(kp, vp, k, k, np.array([0, 64], np.int64))
+
+
+@pytest.mark.parametrize("which", [0, 1])
+def test_three_bit_planes_hold_low_bits_as_two_bit_layout(orc, which):
+    """The low plane of a 3-bit block is exactly a 2-bit block's code section for codes & 3,
+    and the high plane is a bijection of (token, channel) onto its 8192 bits."""
+    rng = np.random.default_rng(33 + which)
+    b3 = np.zeros(orc.block_bytes(3), np.uint8)
+    b2 = np.zeros(orc.block_bytes(2), np.uint8)
+    for o in range(64):
+        codes = rng.integers(0, 8, 128).astype(np.uint8)
+        orc.pack_token(b3, which, 3, o, codes, 0, 0)
+        orc.pack_token(b2, which, 2, o, codes & 3, 0, 0)
+    assert np.array_equal(b3[:2048], b2[:2048])
+    seen = np.zeros(8192, bool)
+    for o in range(64):
+        for c in range(128):
+            blk = np.zeros(orc.block_bytes(3), np.uint8)
+            one = np.zeros(128, np.uint8)
+            one[c] = 4
+            orc.pack_token(blk, which, 3, o, one, 0, 0)
+            bits = np.unpackbits(blk[2048:3072], bitorder="little")
+            assert bits.sum() == 1 and not blk[:2048].any()
+            seen[np.argmax(bits)] = True
+    assert seen.all()
