@@ -24,7 +24,7 @@ _DTYPES = {torch.float32: 0, torch.bfloat16: 1, torch.float16: 2}
 def block_bytes(bits: int) -> int:
     n = int(load().kvq_block_bytes(bits))
     if n == 0:
-        raise ValueError("bits must be 2 or 4")
+        raise ValueError("bits must be 2, 3 or 4")
     return n
 
 

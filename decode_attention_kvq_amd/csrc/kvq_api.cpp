@@ -24,8 +24,8 @@ kvq_status check_cache(const kvq_cache_desc* c, bool need_k, bool need_v) {
   if (c->page_size != 64) return fail(KVQ_ERR_UNSUPPORTED, "page_size must be 64");
   if (c->num_kv_heads < 1) return fail(KVQ_ERR_INVALID_ARG, "num_kv_heads must be >= 1");
   if (c->num_kv_heads > 65535) return fail(KVQ_ERR_UNSUPPORTED, "num_kv_heads must be <= 65535");
-  if ((c->bits_k != 2 && c->bits_k != 4) || (c->bits_v != 2 && c->bits_v != 4))
-    return fail(KVQ_ERR_UNSUPPORTED, "bits_k and bits_v must be 2 or 4");
+  if (c->bits_k < 2 || c->bits_k > 4 || c->bits_v < 2 || c->bits_v > 4)
+    return fail(KVQ_ERR_UNSUPPORTED, "bits_k and bits_v must be 2, 3 or 4");
   if (c->num_pages < 0) return fail(KVQ_ERR_INVALID_ARG, "num_pages must be >= 0");
   if (need_k && !c->k_pages) return fail(KVQ_ERR_INVALID_ARG, "k_pages is null");
   if (need_v && !c->v_pages) return fail(KVQ_ERR_INVALID_ARG, "v_pages is null");
@@ -114,6 +114,8 @@ kvq_status decode_params(const kvq_cache_desc* cache, const void* q, kvq_dtype q
     return fail(KVQ_ERR_INVALID_ARG, "num_q_heads must be a positive multiple of num_kv_heads");
   const int group = num_q_heads / cache->num_kv_heads;
   if (group > 16) return fail(KVQ_ERR_UNSUPPORTED, "at most 16 query heads per KV head");
+  if (cache->bits_k == 3 || cache->bits_v == 3)
+    return fail(KVQ_ERR_UNSUPPORTED, "the read path does not take 3-bit caches yet");
   if (!valid_dtype(q_dtype)) return fail(KVQ_ERR_INVALID_ARG, "unknown query dtype");
   if (max_seq_len < 0 || max_pages < 0) return fail(KVQ_ERR_INVALID_ARG, "max_seq_len and max_pages must be >= 0");
   if ((int64_t)max_pages * 64 < (int64_t)split_length(max_seq_len, win))
@@ -170,7 +172,7 @@ kvq_status check_window(const kvq_cache_desc* cache, const kvq_window_desc* w, b
 extern "C" {
 
 size_t kvq_block_bytes(int32_t bits) {
-  if (bits != 2 && bits != 4) return 0;
+  if (bits < 2 || bits > 4) return 0;
   return (size_t)(64 * 128 * bits / 8 + 4 * 64);
 }
 

@@ -261,6 +261,34 @@ __device__ __forceinline__ void pack_codes(const float* x, const GroupQuant& g, 
   }
 }
 
+// 3-bit codes of the lane's 64 channels (channel 64*hh + j in x[j]) split into the two
+// planes: lo[q] holds (code & 3) of channels 16q .. 16q+15 at bits 2*(j % 16) (a 2-bit
+// word), hb[j / 32] bit j % 32 is bit 2 of channel j's code.
+__device__ __forceinline__ void split_codes3(const float* x, const GroupQuant& g, uint32_t (&lo)[4],
+                                             uint32_t (&hb)[2]) {
+#pragma unroll
+  for (int q = 0; q < 4; ++q) lo[q] = 0u;
+  hb[0] = hb[1] = 0u;
+#pragma unroll
+  for (int j = 0; j < 64; ++j) {
+    const float t = __builtin_amdgcn_fmed3f(code_arg(x[j], g), 0.0f, g.lmax) + 8388608.0f;
+    const uint32_t code = __float_as_uint(t) & 7u;          // 0x4B000000 + code, code <= 7
+    lo[j / 16] |= (code & 3u) << (2 * (j % 16));
+    hb[j / 32] |= (code >> 2) << (j % 32);
+  }
+}
+
+// Key high-plane words of the lane's half row: bit 2 of channel offset u at key_hi_bit(u).
+__device__ __forceinline__ void key_high_words(const uint32_t (&hb)[2], uint32_t (&wh)[2]) {
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    uint32_t w = 0u;
+#pragma unroll
+    for (int u = 0; u < 32; ++u) w |= ((hb[k] >> u) & 1u) << key_hi_bit(u);
+    wh[k] = w;
+  }
+}
+
 // Value of lane (lane ^ d) for d = 1, 2, 4, 8 (d < 16: within a row of 16 lanes).
 template <int D> __device__ __forceinline__ uint32_t xor_lane(uint32_t v) {
   if constexpr (D == 1) return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, false);  // quad [1,0,3,2]
@@ -307,7 +335,9 @@ __device__ __forceinline__ void transpose_codes(uint32_t (&w)[NW], int lane) {
 // token l % 32 and the channel half l / 32.
 // Four resident waves per SIMD (128 VGPRs): measured faster than three despite a few
 // spilled registers, since the waves' loads then overlap other waves' arithmetic.
-template <typename TIn, int KSEL>
+// THREE: the kernel also handles 3-bit codes (compiled separately, so that the 2- and
+// 4-bit kernels keep their register allocation).
+template <typename TIn, int KSEL, bool THREE>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void append_kernel(AppendParams p) {
   // keys: T^T of the head (transform); values: codes as bytes [token][channel] per wave
   constexpr int kTtBytes = kHeadDim * kTtStride * 2;
@@ -389,6 +419,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void a
       uint32_t w[4];
       pack_codes<4, 2>(x, g, w);
       if (valid) *reinterpret_cast<u32x4*>(blk + o * 32 + 16 * hh) = u32x4{w[0], w[1], w[2], w[3]};
+    } else if (THREE && p.bits_k == 3) {
+      uint32_t w[4], hb[2], wh[2];
+      split_codes3(x, g, w, hb);
+      key_high_words(hb, wh);
+      if (valid) {
+        *reinterpret_cast<u32x4*>(blk + o * 32 + 16 * hh) = u32x4{w[0], w[1], w[2], w[3]};
+        *reinterpret_cast<u32x2*>(blk + kLowPlaneBytes + o * 16 + 8 * hh) = u32x2{wh[0], wh[1]};
+      }
     } else {
       uint32_t w[8];
       pack_codes<8, 4>(x, g, w);
@@ -437,6 +475,27 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void a
       uint32_t* dst = words + (o0 / 16 + g16) * kHeadDim + 64 * hh + r;
 #pragma unroll
       for (int k = 0; k < 4; ++k) dst[16 * k] = w[k];
+    } else if (THREE && bits == 3) {
+      uint32_t w[4], hb[2];
+      split_codes3(x, g, w, hb);
+      transpose_codes<2, 4>(w, lane);                       // the low plane as 2-bit codes
+      const int r = lane & 15, g16 = (lane >> 4) & 1;
+      uint32_t* dst = words + (o0 / 16 + g16) * kHeadDim + 64 * hh + r;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) dst[16 * k] = w[k];
+      // high plane: one word per channel holds the wave's 32 tokens.  The ballot of channel
+      // j's bit gives token tl at bit tl (lanes 0-31: channel j, lanes 32-63: channel 64 + j);
+      // lane j keeps both words, and a byte permute moves token t to value_hi_bit(t)
+      uint32_t h0 = 0u, h1 = 0u;
+#pragma unroll
+      for (int j = 0; j < 64; ++j) {
+        const uint64_t bal = __ballot((hb[j / 32] >> (j % 32)) & 1u);
+        h0 = lane == j ? (uint32_t)bal : h0;
+        h1 = lane == j ? (uint32_t)(bal >> 32) : h1;
+      }
+      uint32_t* hw = words + kLowPlaneBytes / 4 + (o0 / 32) * kHeadDim;
+      hw[lane] = __builtin_amdgcn_perm(h0, h0, 0x03010200u);
+      hw[64 + lane] = __builtin_amdgcn_perm(h1, h1, 0x03010200u);
     } else {
       uint32_t w[8];
       pack_codes<8, 4>(x, g, w);
@@ -462,21 +521,29 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void a
     // token by token, the whole wave merges one token's codes into its 128 words (lane l:
     // channels l and l + 64), so each atomic instruction covers contiguous words; the
     // AND/OR merge keeps other tokens' bits of the shared words
-    const int per_word = 32 / bits;
-    const uint32_t fmask = (1u << bits) - 1u;
+    const bool three = THREE && bits == 3;
+    const int per_word = three ? 16 : 32 / bits;              // (3-bit: the low plane)
+    const uint32_t fmask = three ? 3u : (1u << bits) - 1u;
     for (int t = 0; t < kTileTokens; ++t) {
       const int64_t st = __shfl(slot, t);
       if (st < 0 || st >= p.num_pages * kPageTokens) continue;   // same for the whole wave
       const int ot = (int)(st % kPageTokens);
-      const int sh = (ot % per_word) * bits;
-      uint32_t* words = reinterpret_cast<uint32_t*>(p.vpool + ((st / kPageTokens) * p.heads + h) * vbb) +
-                        (ot / per_word) * kHeadDim;
+      const int sh = (ot % per_word) * (three ? 2 : bits);
+      uint8_t* tblk = p.vpool + ((st / kPageTokens) * p.heads + h) * vbb;
+      uint32_t* words = reinterpret_cast<uint32_t*>(tblk) + (ot / per_word) * kHeadDim;
+      uint32_t* hwords = reinterpret_cast<uint32_t*>(tblk + kLowPlaneBytes) + (ot / 32) * kHeadDim;
+      const int hb = value_hi_bit(ot % 32);
 #pragma unroll
       for (int half = 0; half < 2; ++half) {
         const int c = lane + 64 * half;
-        const uint32_t code = (vb[t * 32 + c / 4] >> (8 * (c % 4))) & fmask;
+        const uint32_t full = vb[t * 32 + c / 4] >> (8 * (c % 4));
+        const uint32_t code = full & fmask;
         atomicAnd(words + c, ~(fmask << sh));
         atomicOr(words + c, code << sh);
+        if (three) {                           // bit 2 into the high plane
+          atomicAnd(hwords + c, ~(1u << hb));
+          atomicOr(hwords + c, ((full >> 2) & 1u) << hb);
+        }
       }
     }
   }
@@ -508,12 +575,14 @@ hipError_t launch_typed(const AppendParams& p, hipStream_t stream) {
     return hipGetLastError();
   }
   const dim3 grid((unsigned)((p.n + kBlockTokens - 1) / kBlockTokens), (unsigned)p.heads, 2u), block(256);
-  if (ksel == 3) {
-    hipLaunchKernelGGL((append_kernel<TIn, 3>), grid, block, 0, stream, p);
-  } else if (ksel == 8) {
-    hipLaunchKernelGGL((append_kernel<TIn, 8>), grid, block, 0, stream, p);
+  if (p.bits_k == 3 || p.bits_v == 3) {
+    if (ksel == 3) hipLaunchKernelGGL((append_kernel<TIn, 3, true>), grid, block, 0, stream, p);
+    else if (ksel == 8) hipLaunchKernelGGL((append_kernel<TIn, 8, true>), grid, block, 0, stream, p);
+    else hipLaunchKernelGGL((append_kernel<TIn, 0, true>), grid, block, 0, stream, p);
   } else {
-    hipLaunchKernelGGL((append_kernel<TIn, 0>), grid, block, 0, stream, p);
+    if (ksel == 3) hipLaunchKernelGGL((append_kernel<TIn, 3, false>), grid, block, 0, stream, p);
+    else if (ksel == 8) hipLaunchKernelGGL((append_kernel<TIn, 8, false>), grid, block, 0, stream, p);
+    else hipLaunchKernelGGL((append_kernel<TIn, 0, false>), grid, block, 0, stream, p);
   }
   return hipGetLastError();
 }

@@ -8,7 +8,7 @@
 namespace kvq {
 namespace {
 
-// One thread per (token, head, 4 channels).
+// One thread per (token, head, 4 channels).  3-bit codes are read from their two planes.
 __global__ __launch_bounds__(256) void dequant_kernel(DequantParams p) {
   const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   const int64_t total = p.n * p.heads * (kHeadDim / 4);
@@ -32,8 +32,20 @@ __global__ __launch_bounds__(256) void dequant_kernel(DequantParams p) {
   for (int e = 0; e < 4; ++e) {
     const int c = 4 * c4 + e;
     uint32_t code;
-    if (p.which == 0) code = (words[o * (kHeadDim / per_word) + c / per_word] >> ((c % per_word) * bits)) & mask;
-    else code = (words[(o / per_word) * kHeadDim + c] >> ((o % per_word) * bits)) & mask;
+    if (bits == 3) {
+      const uint32_t* hi = words + kLowPlaneBytes / 4;
+      if (p.which == 0) {
+        code = ((words[o * 8 + c / 16] >> (2 * (c % 16))) & 3u) |
+               (((hi[o * 4 + c / 32] >> key_hi_bit(c % 32)) & 1u) << 2);
+      } else {
+        code = ((words[(o / 16) * kHeadDim + c] >> (2 * (o % 16))) & 3u) |
+               (((hi[(o / 32) * kHeadDim + c] >> value_hi_bit(o % 32)) & 1u) << 2);
+      }
+    } else if (p.which == 0) {
+      code = (words[o * (kHeadDim / per_word) + c / per_word] >> ((c % per_word) * bits)) & mask;
+    } else {
+      code = (words[(o / per_word) * kHeadDim + c] >> ((o % per_word) * bits)) & mask;
+    }
     r[e] = __builtin_fmaf((float)code, sf, zf);
   }
   *reinterpret_cast<f32x4*>(p.out + (i * p.heads + h) * kHeadDim + 4 * c4) = r;

@@ -21,6 +21,18 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 __host__ __device__ constexpr int code_bytes(int bits) { return kPageTokens * kHeadDim * bits / 8; }
 __host__ __device__ constexpr int block_bytes(int bits) { return code_bytes(bits) + 4 * kPageTokens; }
 
+// 3-bit codes are two bit planes.  The low plane (bits 0-1 of every code) is laid out as a
+// 2-bit code section; the high plane (bit 2) follows it, at byte kLowPlaneBytes:
+//   keys    token o's 128 bits are the words o*4 + c/32, channel offset u = c % 32 at bit
+//           key_hi_bit(u) (so that shifts and one AND put 8 of them at bit 2 of fp4 nibbles
+//           in the order the 2-bit plane gives its codes)
+//   values  word (o/32)*128 + c holds tokens 32*(o/32) .. +31 of channel c, token offset
+//           t = o % 32 at bit value_hi_bit(t) (a 16-token run of one lane group sits in one
+//           byte of each 16-bit half)
+constexpr int kLowPlaneBytes = code_bytes(2);
+__host__ __device__ constexpr int key_hi_bit(int u) { return 4 * ((u % 16) / 2) + 2 * (u / 16) + u % 2; }
+__host__ __device__ constexpr int value_hi_bit(int t) { return t % 8 + 16 * ((t / 8) % 2) + 8 * (t / 16); }
+
 // fp32 -> fp16 bits with the hardware conversion (operands of matrix-core products,
 // where the last rounding bit does not matter).
 __device__ __forceinline__ uint16_t f32_to_f16_bits(float x) {

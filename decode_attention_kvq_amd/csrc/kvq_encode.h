@@ -221,7 +221,38 @@ __device__ __forceinline__ void small_quantize_store(float a, float b, bool is_v
     uint16_t* meta = reinterpret_cast<uint16_t*>(blk + code_bytes(bits));
     meta[lane * kPageTokens + o] = lane ? g.z16 : g.s16;
   }
-  if (!is_v) {
+  if (bits == 3) {
+    if (!is_v) {
+      // low plane: the 2-bit token row of (code & 3); high plane: bit 2 of both channels at
+      // key_hi_bit of their offsets, OR-ed over the 16 lanes of a word (quads, half-row
+      // mirror, row mirror)
+      uint32_t wl = ((code_a & 3u) | ((code_b & 3u) << 2)) << (4 * (lane % 8));
+      wl |= (uint32_t)__builtin_amdgcn_mov_dpp((int)wl, 0xB1, 0xF, 0xF, false);
+      wl |= (uint32_t)__builtin_amdgcn_mov_dpp((int)wl, 0x4E, 0xF, 0xF, false);
+      wl |= (uint32_t)__builtin_amdgcn_mov_dpp((int)wl, 0x141, 0xF, 0xF, false);
+      uint32_t wh = ((code_a >> 2) | ((code_b >> 2) << 1)) << key_hi_bit((2 * lane) % 32);
+      wh |= (uint32_t)__builtin_amdgcn_mov_dpp((int)wh, 0xB1, 0xF, 0xF, false);
+      wh |= (uint32_t)__builtin_amdgcn_mov_dpp((int)wh, 0x4E, 0xF, 0xF, false);
+      wh |= (uint32_t)__builtin_amdgcn_mov_dpp((int)wh, 0x141, 0xF, 0xF, false);
+      wh |= (uint32_t)__builtin_amdgcn_mov_dpp((int)wh, 0x140, 0xF, 0xF, false);
+      if (lane % 8 == 0) reinterpret_cast<uint32_t*>(blk + o * 32)[lane / 8] = wl;
+      if (lane % 16 == 0) reinterpret_cast<uint32_t*>(blk + kLowPlaneBytes + o * 16)[lane / 16] = wh;
+    } else {
+      // low plane words (o/16)*128 + c at bit 2*(o%16); high plane words (o/32)*128 + c at
+      // value_hi_bit(o%32); other tokens' bits are kept
+      const int sh = 2 * (o % 16), hb = value_hi_bit(o % 32);
+      uint32_t* wl = reinterpret_cast<uint32_t*>(blk) + (o / 16) * kHeadDim + 2 * lane;
+      uint32_t* wh = reinterpret_cast<uint32_t*>(blk + kLowPlaneBytes) + (o / 32) * kHeadDim + 2 * lane;
+      atomicAnd(wl, ~(3u << sh));
+      atomicOr(wl, (code_a & 3u) << sh);
+      atomicAnd(wl + 1, ~(3u << sh));
+      atomicOr(wl + 1, (code_b & 3u) << sh);
+      atomicAnd(wh, ~(1u << hb));
+      atomicOr(wh, (code_a >> 2) << hb);
+      atomicAnd(wh + 1, ~(1u << hb));
+      atomicOr(wh + 1, (code_b >> 2) << hb);
+    }
+  } else if (!is_v) {
     // token row: word w of 32/bits channels; lane l's pair sits at bits 2*bits*(l % (16/bits))
     const int lpw = 16 / bits;                  // lanes per word
     uint32_t wv = (code_a | (code_b << bits)) << (2 * bits * (lane % lpw));

@@ -71,12 +71,12 @@ def _desc(**kw):
 
 def test_block_bytes_and_status_strings(lib):
     assert lib.kvq_block_bytes(2) == 2304 and lib.kvq_block_bytes(4) == 4352
-    assert lib.kvq_block_bytes(3) == 0
+    assert lib.kvq_block_bytes(3) == 3328 and lib.kvq_block_bytes(5) == 0
     assert lib.kvq_status_string(-3) == b"workspace too small"
 
 
 @pytest.mark.parametrize("kw,status", [
-    (dict(head_dim=64), -2), (dict(page_size=32), -2), (dict(bits_k=3), -2), (dict(bits_v=8), -2),
+    (dict(head_dim=64), -2), (dict(page_size=32), -2), (dict(bits_k=5), -2), (dict(bits_v=8), -2),
     (dict(num_kv_heads=0), -1), (dict(p_lo=0.5, p_hi=0.4), -1), (dict(p_hi=1.5), -1),
     (dict(quant_k=1, alpha_k=0.0), -1), (dict(quant_v=7), -1), (dict(k_pages=0), -1),
 ])

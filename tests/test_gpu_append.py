@@ -67,7 +67,7 @@ def _run_both(k, v, slots, num_pages, H, bits, quant, rng, t=None, t_oracle="sam
 # Batches of up to 512 tokens take the one-token-per-workgroup path, larger ones the
 # 128-token-tile path: each test runs a size on both sides of that boundary.
 @pytest.mark.parametrize("n", [300, 700])
-@pytest.mark.parametrize("bits", [(2, 2), (4, 4), (2, 4)])
+@pytest.mark.parametrize("bits", [(2, 2), (4, 4), (2, 4), (3, 3), (3, 2), (4, 3)])
 @pytest.mark.parametrize("quant", [("percentile", "percentile"), ("rms", "rms"), ("percentile", "rms")])
 @pytest.mark.parametrize("layout", ["aligned", "scattered"])
 def test_stage_a_bit_exact(bits, quant, layout, n):
@@ -120,7 +120,7 @@ def test_append_one_token_at_a_time_preserves_neighbours():
 
 @pytest.mark.parametrize("n", [512, 1024])
 @pytest.mark.parametrize("dtype", ["bf16", "f16"])
-@pytest.mark.parametrize("bits", [(2, 2), (4, 4)])
+@pytest.mark.parametrize("bits", [(2, 2), (4, 4), (3, 3)])
 def test_stage_b_transform_on_matrix_cores(dtype, bits, n):
     """n = 512: fp32 transform, one token per workgroup; n = 1024: matrix-core transform."""
     rng = np.random.default_rng(13)
@@ -176,7 +176,7 @@ def test_f32_transform_tiny_config():
     assert np.sum(gc != oc) <= 4, np.sum(gc != oc)
 
 
-@pytest.mark.parametrize("bits", [2, 4])
+@pytest.mark.parametrize("bits", [2, 3, 4])
 @pytest.mark.parametrize("which", [0, 1])
 def test_dequant_bit_exact(bits, which):
     rng = np.random.default_rng(16 + bits + which)
