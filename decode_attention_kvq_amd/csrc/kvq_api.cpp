@@ -114,8 +114,6 @@ kvq_status decode_params(const kvq_cache_desc* cache, const void* q, kvq_dtype q
     return fail(KVQ_ERR_INVALID_ARG, "num_q_heads must be a positive multiple of num_kv_heads");
   const int group = num_q_heads / cache->num_kv_heads;
   if (group > 16) return fail(KVQ_ERR_UNSUPPORTED, "at most 16 query heads per KV head");
-  if (cache->bits_k == 3 || cache->bits_v == 3)
-    return fail(KVQ_ERR_UNSUPPORTED, "the read path does not take 3-bit caches yet");
   if (!valid_dtype(q_dtype)) return fail(KVQ_ERR_INVALID_ARG, "unknown query dtype");
   if (max_seq_len < 0 || max_pages < 0) return fail(KVQ_ERR_INVALID_ARG, "max_seq_len and max_pages must be >= 0");
   if ((int64_t)max_pages * 64 < (int64_t)split_length(max_seq_len, win))

@@ -136,6 +136,7 @@ __host__ __device__ constexpr int k2_channel(int kg, int j) {
   return 32 * kg + 16 * (j / 16) + 2 * (j % 8) + (j / 8) % 2;
 }
 constexpr uint32_t kFp4CodeMask = 0x33333333u;
+constexpr uint32_t kFp4HighMask = 0x44444444u;   // bit 2 of every nibble: the fp4 value 2
 constexpr int kQTerms = 3;          // fp6 terms of q'': about 12 significant bits together
 
 typedef int v8i __attribute__((ext_vector_type(8)));
@@ -181,13 +182,19 @@ constexpr int kStreamPolicy = 2;   // gfx950 CPol NT bit
 // Pages in flight per wave: a register ring of PIPE pages.
 template <int BK, int BV> constexpr int pipe_depth() { return BK + BV <= 4 ? 3 : 2; }
 
+// 3-bit codes are a 2-bit low plane plus a 1-bit high plane: everything the low plane
+// needs is the 2-bit machinery (plane width of the low plane).
+template <int B> constexpr int low_bits() { return B == 3 ? 2 : B; }
+
 // A page's K and V blocks as seen by one lane, loaded straight into the registers the
 // matrix-core operands are built from.  A = accumulators (GP/4) of score rows per lane.
 template <int BK, int BV, int A> struct PageRegs {
-  typedef std::conditional_t<BK == 2, u32x2, u32x4> KRow;
-  KRow k[4];                   // K codes of tile t4: 32 channels of the lane's token
-  u32x4 v[BV == 2 ? 2 : 4];    // V codes: the lane's V row(s), two 16 B halves each
+  typedef std::conditional_t<BK == 4, u32x4, u32x2> KRow;
+  KRow k[4];                   // K codes of tile t4: 32 channels of the lane's token (low plane)
+  u32x4 v[BV == 4 ? 4 : 2];    // V codes: the lane's V row(s), two 16 B halves each (low plane)
   u32x2 meta[A][4];            // fp16 (s_k, z_k, s_v, z_v) of the lane's 4 tokens per row group
+  uint32_t kh[BK == 3 ? 4 : 1];   // 3-bit keys: high-plane bits of the 32 channels, per tile
+  u32x4 vh[BV == 3 ? 2 : 1];      // 3-bit values: high-plane words of the lane's channels
 };
 
 // Buffer resource of one 128-channel block: loads past num_records bytes return zero and
@@ -198,7 +205,7 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t block_rsrc(const uint8_t* base
 
 // Per-lane byte offsets inside a block (the same for every page).
 template <int BK, int BV, int A> struct LaneOffsets {
-  int k, v, meta[A];
+  int k, v, meta[A], kh, vh;
 };
 
 template <int BK, int BV, int A>
@@ -206,13 +213,21 @@ __device__ __forceinline__ void load_page(PageRegs<BK, BV, A>& r, __amdgpu_buffe
                                           __amdgpu_buffer_rsrc_t rv, const LaneOffsets<BK, BV, A>& o) {
 #pragma unroll
   for (int t4 = 0; t4 < 4; ++t4) {
-    if constexpr (BK == 2) r.k[t4] = __builtin_amdgcn_raw_buffer_load_b64(rk, o.k + 128 * t4, 0, kStreamPolicy);
+    if constexpr (BK != 4) r.k[t4] = __builtin_amdgcn_raw_buffer_load_b64(rk, o.k + 128 * t4, 0, kStreamPolicy);
     else r.k[t4] = __builtin_amdgcn_raw_buffer_load_b128(rk, o.k + 256 * t4, 0, kStreamPolicy);
   }
+  if constexpr (BK == 3) {
 #pragma unroll
-  for (int rr = 0; rr < (BV == 2 ? 1 : 2); ++rr) {
+    for (int t4 = 0; t4 < 4; ++t4) r.kh[t4] = __builtin_amdgcn_raw_buffer_load_b32(rk, o.kh + 64 * t4, 0, kStreamPolicy);
+  }
+#pragma unroll
+  for (int rr = 0; rr < (BV == 4 ? 2 : 1); ++rr) {
     r.v[2 * rr] = __builtin_amdgcn_raw_buffer_load_b128(rv, o.v + 512 * rr, 0, kStreamPolicy);
     r.v[2 * rr + 1] = __builtin_amdgcn_raw_buffer_load_b128(rv, o.v + 512 * rr + 256, 0, kStreamPolicy);
+  }
+  if constexpr (BV == 3) {
+    r.vh[0] = __builtin_amdgcn_raw_buffer_load_b128(rv, o.vh, 0, kStreamPolicy);
+    r.vh[1] = __builtin_amdgcn_raw_buffer_load_b128(rv, o.vh + 256, 0, kStreamPolicy);
   }
 #pragma unroll
   for (int a = 0; a < A; ++a) {
@@ -248,6 +263,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
   constexpr int A = GP / 4;          // score accumulators (tiles per column)
   constexpr int PIPE = pipe_depth<BK, BV>();
   constexpr int KB = block_bytes(BK), VB = block_bytes(BV);
+  constexpr int BVL = low_bits<BV>();   // low-plane width of the values
   const int chunk = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int kg = lane >> 4, n = lane & 15;
@@ -281,8 +297,12 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
   LaneOffsets<BK, BV, A> lo;
   {
     const int tok0 = 16 * (n >> 2) + (n & 3);
-    lo.k = BK == 2 ? tok0 * 32 + kg * 8 : tok0 * 64 + kg * 16;
-    lo.v = (BV == 2 ? kg : 2 * kg) * kHeadDim * 4 + n * 16;
+    lo.k = BK != 4 ? tok0 * 32 + kg * 8 : tok0 * 64 + kg * 16;
+    lo.v = (BV != 4 ? kg : 2 * kg) * kHeadDim * 4 + n * 16;
+    // high planes: the token's 16-byte key row (4 bytes per lane group); the value words of
+    // the lane's channels in the 32-token row that holds its lane group's 16 tokens
+    lo.kh = kLowPlaneBytes + tok0 * 16 + kg * 4;
+    lo.vh = kLowPlaneBytes + (kg / 2) * kHeadDim * 4 + n * 16;
 #pragma unroll
     for (int a = 0; a < A; ++a) lo.meta[a] = 2 * (16 * kg + 4 * (a * NB + beta));
   }
@@ -370,9 +390,9 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
   // The product with the fp4 codes (value c/2) gives half of q'.code: F = 2.
   v8i bq6[kQTerms];
   int sreg[kQTerms];
-  u32x4 bq[BK == 2 ? 1 : NB][4];     // fp16 operands (4-bit keys)
+  u32x4 bq[BK != 4 ? 1 : NB][4];     // fp16 operands (4-bit keys)
   const int gq = n % GP;
-  if constexpr (BK == 2) {
+  if constexpr (BK != 4) {
     uint8_t* qcode = smem;                                         // [term][head][channel]
     uint32_t* qpack = reinterpret_cast<uint32_t*>(smem + kQTerms * GP * kHeadDim);  // [term][kg][head][6]
     int* qexp = reinterpret_cast<int*>(qpack + kQTerms * 4 * GP * 6);
@@ -495,14 +515,24 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
       int e = 0;
 #pragma unroll
       for (int bb = 0; bb < NB; ++bb)
-        if (beta == bb) e = v_token_class<BV>(4 * (a * NB + bb) + r);
-      vcls[a][r] = BV * e;
+        if (beta == bb) e = v_token_class<BVL>(4 * (a * NB + bb) + r);
+      vcls[a][r] = BVL * e;
     }
+  // 3-bit values: the high-plane bit of lane-group token u is the subnormal fp16
+  // 2^(u % 8) * 2^-24 and weighs 4 (code = low + 4 * high), so its P~ is the low plane's
+  // times 4 * 2^(vcls - u % 8); the high words of odd lane groups hold their tokens one
+  // byte up in each half
+  float hfac[A][4];
+#pragma unroll
+  for (int a = 0; a < A; ++a)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) hfac[a][r] = ldexpf(4.0f, vcls[a][r] - (4 * (a * NB + beta) + r) % 8);
+  const int hsh = 8 * (kg & 1);
   // halves of the P.V operand words that carry this lane's tiles (see the P.V step)
   uint32_t bmask[2];
 #pragma unroll
   for (int s = 0; s < 2; ++s) {
-    const int t_lo = v_token<BV>(s, 0) / 4, t_hi = v_token<BV>(s, 1) / 4;   // same for every jj
+    const int t_lo = v_token<BVL>(s, 0) / 4, t_hi = v_token<BVL>(s, 1) / 4;   // same for every jj
     bmask[s] = ((t_lo % NB == beta) ? 0x0000FFFFu : 0u) | ((t_hi % NB == beta) ? 0xFFFF0000u : 0u);
   }
   float m = -__builtin_inff();   // running max of x' for this lane's column
@@ -517,7 +547,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
     f32x4 sacc[A];
 #pragma unroll
     for (int a = 0; a < A; ++a) sacc[a] = f32x4{};
-    if constexpr (BK == 2) {
+    if constexpr (BK != 4) {
       // one 16x16x128 product per tile and fp6 term; the op_sel'd scale byte keeps tile t4
       // out of every column block but t4 % NB
 #pragma unroll
@@ -527,6 +557,16 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
                         (int)((w1 >> 2) & kFp4CodeMask), 0, 0, 0, 0};
 #pragma unroll
         for (int k = 0; k < kQTerms; ++k) sacc[t4 / NB] = mma_fp4_fp6(t4 % NB, av, bq6[k], sacc[t4 / NB], sreg[k]);
+        if constexpr (BK == 3) {
+          // high plane: operand element (dword d, nibble i) is channel offset
+          // 16(d/2) + d%2 + 2i, whose bit sits at 4i + d; shifted to bit 2 of the nibble it
+          // is the fp4 value 2 = (4 * bit) / 2, so the two products add to code / 2
+          const uint32_t h = pr.kh[t4];
+          const v8i ah = {(int)((h << 2) & kFp4HighMask), (int)((h << 1) & kFp4HighMask), (int)(h & kFp4HighMask),
+                          (int)((h >> 1) & kFp4HighMask), 0, 0, 0, 0};
+#pragma unroll
+          for (int k = 0; k < kQTerms; ++k) sacc[t4 / NB] = mma_fp4_fp6(t4 % NB, ah, bq6[k], sacc[t4 / NB], sreg[k]);
+        }
       }
     } else
 #pragma unroll
@@ -598,7 +638,8 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
     const int svbits = col_max_i((int)svm);
     const int e16 = (svbits >> 10) & 0x1F;
     const int ev = svbits == 0 ? -30 : (e16 == 0 ? -15 : e16 - 15);
-    const int S_tight = 14 - (int)kLag - ev;
+    // (3-bit values: the high plane's P~ carries up to 4x more, two bits of headroom)
+    const int S_tight = (BV == 3 ? 12 : 14) - (int)kLag - ev;
     const bool need_s = S_tight < S;
     const int S_new = need_s ? S_tight - kSMargin : S;
     const bool need_m = F * (mx - m) > kLag;       // false when the column has no token here
@@ -638,7 +679,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
     for (int s = 0; s < 2; ++s)
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj) {
-        const int t_lo = v_token<BV>(s, 2 * jj) / 4, t_hi = v_token<BV>(s, 2 * jj + 1) / 4;
+        const int t_lo = v_token<BVL>(s, 2 * jj) / 4, t_hi = v_token<BVL>(s, 2 * jj + 1) / 4;
         if constexpr (NB == 1) {
           bp[s][jj] = pack_f16x2(pt[t_lo][jj], pt[t_hi][jj]);
         } else {
@@ -649,7 +690,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
         }
       }
 #pragma unroll
-    for (int rr = 0; rr < (BV == 2 ? 1 : 2); ++rr) {
+    for (int rr = 0; rr < (BV != 4 ? 1 : 2); ++rr) {
       const u32x4 va = pr.v[2 * rr], vc = pr.v[2 * rr + 1];
 #pragma unroll
       for (int mt = 0; mt < 8; ++mt) {
@@ -657,11 +698,40 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
         for (int s = 0; s < 2; ++s) {
           if (BV == 4 && s != rr) continue;
           const uint32_t w = (mt >> 2) ? vc[mt & 3] : va[mt & 3];
-          const uint32_t ws = shifted<BV>(w);
+          const uint32_t ws = shifted<BVL>(w);
           u32x4 av;
 #pragma unroll
-          for (int jj = 0; jj < 4; ++jj) av[jj] = code_pair<BV>(w, ws, BV == 2 ? 4 * s + jj : jj);
+          for (int jj = 0; jj < 4; ++jj) av[jj] = code_pair<BVL>(w, ws, BVL == 2 ? 4 * s + jj : jj);
           acc_o[mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(av), as_half8(bp[s]), acc_o[mt], 0, 0, 0);
+        }
+      }
+    }
+    if constexpr (BV == 3) {
+      // high plane: token pair (p, p + 8), p = 4s + jj, sits at bits p and 16 + p of the
+      // lane group's (aligned) word, the same pairs as the low plane's operand
+      u32x4 bph[2];
+#pragma unroll
+      for (int s = 0; s < 2; ++s)
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+          const int t_lo = v_token<2>(s, 2 * jj) / 4, t_hi = v_token<2>(s, 2 * jj + 1) / 4;
+          if constexpr (NB == 1) {
+            bph[s][jj] = pack_f16x2(pt[t_lo][jj] * hfac[t_lo][jj], pt[t_hi][jj] * hfac[t_hi][jj]);
+          } else {
+            const uint32_t both = pack_f16x2(pt[t_lo / NB][jj] * hfac[t_lo / NB][jj],
+                                             pt[t_hi / NB][jj] * hfac[t_hi / NB][jj]);
+            bph[s][jj] = both & bmask[s];
+          }
+        }
+#pragma unroll
+      for (int mt = 0; mt < 8; ++mt) {
+        const uint32_t wh = ((mt >> 2) ? pr.vh[1][mt & 3] : pr.vh[0][mt & 3]) >> hsh;
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+          u32x4 av;
+#pragma unroll
+          for (int jj = 0; jj < 4; ++jj) av[jj] = wh & ((1u << (4 * s + jj)) | (1u << (16 + 4 * s + jj)));
+          acc_o[mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(av), as_half8(bph[s]), acc_o[mt], 0, 0, 0);
         }
       }
     }
@@ -811,10 +881,17 @@ DecodeSplit decode_split(int batch, int heads_kv, int max_seq_len) {
 }
 
 hipError_t launch_decode(const DecodeParams& p, int bits_k, int bits_v, int q_dtype, hipStream_t stream) {
-  if (bits_k == 2 && bits_v == 2) return launch_bits<2, 2>(p, q_dtype, stream);
-  if (bits_k == 2 && bits_v == 4) return launch_bits<2, 4>(p, q_dtype, stream);
-  if (bits_k == 4 && bits_v == 2) return launch_bits<4, 2>(p, q_dtype, stream);
-  return launch_bits<4, 4>(p, q_dtype, stream);
+  switch (bits_k * 10 + bits_v) {
+    case 22: return launch_bits<2, 2>(p, q_dtype, stream);
+    case 23: return launch_bits<2, 3>(p, q_dtype, stream);
+    case 24: return launch_bits<2, 4>(p, q_dtype, stream);
+    case 32: return launch_bits<3, 2>(p, q_dtype, stream);
+    case 33: return launch_bits<3, 3>(p, q_dtype, stream);
+    case 34: return launch_bits<3, 4>(p, q_dtype, stream);
+    case 42: return launch_bits<4, 2>(p, q_dtype, stream);
+    case 43: return launch_bits<4, 3>(p, q_dtype, stream);
+    default: return launch_bits<4, 4>(p, q_dtype, stream);
+  }
 }
 
 }  // namespace kvq

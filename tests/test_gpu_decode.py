@@ -58,7 +58,7 @@ def _oracle_cache(rng, B, H, seq, bits, config=1, t=None, quant=("percentile", "
     return kp, vp, bt
 
 
-@pytest.mark.parametrize("bits", [(2, 2), (4, 4), (2, 4), (4, 2)])
+@pytest.mark.parametrize("bits", [(2, 2), (4, 4), (2, 4), (4, 2), (3, 3), (3, 2), (2, 3), (4, 3), (3, 4)])
 @pytest.mark.parametrize("group", [1, 4, 8, 16])
 def test_stage_c_oracle_cache(bits, group):
     rng = np.random.default_rng(100 + 10 * bits[0] + bits[1] + group)
@@ -88,6 +88,58 @@ def test_stage_c_random_codes_and_empty_sequences(q_dtype):
     ref = oracle.decode_attention(kp, vp, q, bt, seq, bits_k=2, bits_v=4)
     assert np.all(got[0] == 0)
     err = row_rel_err(got[1:], ref[1:])
+    assert err.max() <= TOL, err.max()
+
+
+@pytest.mark.parametrize("bits,q_dtype", [((3, 3), "f32"), ((3, 2), "f16"), ((2, 3), "bf16")])
+def test_three_bit_random_codes_split_and_empty(bits, q_dtype):
+    """3-bit planes of random bytes (every high-plane bit pattern), ragged and empty
+    sequences, one sequence split over several workgroups."""
+    rng = np.random.default_rng(17 + bits[0] + bits[1])
+    B, H, G = 4, 2, 4
+    seq = np.array([0, 97, 4500, 64], np.int32)
+    pps = 71
+    num_pages = B * pps
+    kp = synth.random_packed_pool(rng, num_pages, H, bits[0])
+    vp = synth.random_packed_pool(rng, num_pages, H, bits[1])
+    bt = synth.shuffled_block_table(B, pps, num_pages, rng)
+    q = synth.to_dtype(rng.standard_normal((B, H * G, 128)).astype(np.float32) * 3, q_dtype)
+    got = _gpu_decode(kp, vp, q, bt, seq, bits, q_dtype=q_dtype, max_seq_len=4500)
+    ref = oracle.decode_attention(kp, vp, q, bt, seq, bits_k=bits[0], bits_v=bits[1])
+    assert np.all(got[0] == 0)
+    err = row_rel_err(got[1:], ref[1:])
+    assert err.max() <= TOL, err.max()
+
+
+@pytest.mark.parametrize("bits", [(3, 3), (4, 3)])
+def test_three_bit_end_to_end(bits):
+    """GPU write path then GPU read path against the oracle's, bf16 inputs with a transform."""
+    rng = np.random.default_rng(19 + bits[0])
+    B, H, G = 3, 2, 4
+    seq = np.array([700, 65, 1300], np.int32)
+    pps = int(-(-seq.max() // 64))
+    num_pages = B * pps + 2
+    bt = synth.shuffled_block_table(B, pps, num_pages, rng)
+    slots = synth.slots_for(bt, seq)
+    w = synth.Workload("t", 1, H * G, H, B, len(slots), bits[0], bits[1], "percentile", "bf16", True)
+    k, v = synth.kv_tokens(w, len(slots))
+    t, tinv = _transforms(1, H, G)
+    cache = api.KVCache(num_pages, H, bits[0], bits[1])
+    api.kvq_quantize_append(cache, torch.from_numpy(k).to(torch.bfloat16).cuda(),
+                            torch.from_numpy(v).to(torch.bfloat16).cuda(), torch.from_numpy(slots).cuda(),
+                            t_k=torch.from_numpy(t).to(torch.bfloat16).cuda())
+    q = synth.decode_queries(w)
+    out = api.kvq_decode_attn(cache, torch.from_numpy(q).to(torch.bfloat16).cuda(), torch.from_numpy(bt).cuda(),
+                              torch.from_numpy(seq).cuda(), int(seq.max()), t_k_inv_t=torch.from_numpy(tinv).cuda())
+    torch.cuda.synchronize()
+    kp, vp = oracle.new_pool(num_pages, H, bits[0]), oracle.new_pool(num_pages, H, bits[1])
+    oracle.append(kp, vp, k, v, slots, t_k=t, bits_k=bits[0], bits_v=bits[1])
+    assert np.array_equal(cache.v_pages.cpu().numpy(), vp)
+    ref = oracle.decode_attention(kp, vp, q, bt, seq, t_inv_t=tinv, bits_k=bits[0], bits_v=bits[1])
+    got_c = _gpu_decode(kp, vp, q, bt, seq, bits, tinv=tinv, q_dtype="bf16")
+    assert row_rel_err(got_c, ref).max() <= TOL
+    vmax = np.abs(oracle.dequant(vp, 1, bits[1], slots)).max(axis=0).max(axis=-1)
+    err = np.max(np.abs(out.cpu().numpy() - ref), axis=-1) / np.repeat(vmax, G)[None]
     assert err.max() <= TOL, err.max()
 
 

@@ -194,6 +194,8 @@ STEP_CASES = [
     # batch x flush > 512 candidate positions: the flush runs on the 128-token tile kernel
     Case(4, 8, 64, [50, 60, 70, 100, 120, 130, 140, 75, 200], (2, 2), "bf16", False, 4),
     Case(4, 8, 64, [50, 60, 70, 100, 120, 130, 140, 75, 200], (4, 4), "f16", True, 4, rows_perm=True),
+    Case(3, 10, 8, [0, 5, 20, 40], (3, 3), "bf16", False, 4),
+    Case(4, 8, 64, [50, 60, 70, 100, 120, 130, 140, 75, 200], (3, 2), "bf16", True, 8),
 ]
 
 
