@@ -315,7 +315,7 @@ def main():
     del s
     torch.cuda.empty_cache()
     if args.extra:
-        for name in ("qwen3-8b-b1-16k", "long-b16-128k-quest"):
+        for name in ("qwen3-8b-b1-16k", "long-b16-128k-quest", "qwen3-8b-b64-16k-3bit"):
             w2 = synth.WORKLOADS[name]
             s2 = setup_decode(w2, torch, api, calib, synth, dev)
             t2 = time_steps(w2, s2, torch, api, 20, 10)
@@ -326,7 +326,7 @@ def main():
                            "decode_frac": dby / (t2["decode"] * 1e-3) / HBM_PEAK}
             del s2
             torch.cuda.empty_cache()
-        for name in ("prefill-8x32k-4bit", "prefill-8x32k-2bit"):
+        for name in ("prefill-8x32k-4bit", "prefill-8x32k-2bit", "prefill-8x32k-3bit"):
             extra[name] = time_prefill(synth.WORKLOADS[name], torch, api, calib, synth, dev)
         rec["other_workloads"] = extra
     if not args.no_cpu_baseline:

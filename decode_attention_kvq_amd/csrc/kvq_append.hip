@@ -278,14 +278,20 @@ __device__ __forceinline__ void split_codes3(const float* x, const GroupQuant& g
   }
 }
 
-// Key high-plane words of the lane's half row: bit 2 of channel offset u at key_hi_bit(u).
-__device__ __forceinline__ void key_high_words(const uint32_t (&hb)[2], uint32_t (&wh)[2]) {
+// The same for a key half row, with the high-plane words of the row built directly:
+// bit 2 of channel offset u = j % 32 at key_hi_bit(u) of wh[j / 32].
+__device__ __forceinline__ void split_codes3_key(const float* x, const GroupQuant& g, uint32_t (&lo)[4],
+                                                 uint32_t (&wh)[2]) {
 #pragma unroll
-  for (int k = 0; k < 2; ++k) {
-    uint32_t w = 0u;
+  for (int q = 0; q < 4; ++q) lo[q] = 0u;
+  wh[0] = wh[1] = 0u;
 #pragma unroll
-    for (int u = 0; u < 32; ++u) w |= ((hb[k] >> u) & 1u) << key_hi_bit(u);
-    wh[k] = w;
+  for (int j = 0; j < 64; ++j) {
+    const float t = __builtin_amdgcn_fmed3f(code_arg(x[j], g), 0.0f, g.lmax) + 8388608.0f;
+    const uint32_t code = __float_as_uint(t) & 7u;
+    lo[j / 16] |= (code & 3u) << (2 * (j % 16));
+    const int hbit = key_hi_bit(j % 32);
+    wh[j / 32] |= hbit >= 2 ? (code & 4u) << (hbit - 2) : (code & 4u) >> (2 - hbit);
   }
 }
 
@@ -295,6 +301,7 @@ template <int D> __device__ __forceinline__ uint32_t xor_lane(uint32_t v) {
   if constexpr (D == 2) return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x4E, 0xF, 0xF, false);  // quad [2,3,0,1]
   if constexpr (D == 4) return (uint32_t)__builtin_amdgcn_ds_swizzle((int)v, (4 << 10) | 0x1F);    // xor 4
   if constexpr (D == 8) return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x128, 0xF, 0xF, false); // row rotate 8
+  if constexpr (D == 16) return (uint32_t)__builtin_amdgcn_ds_swizzle((int)v, (16 << 10) | 0x1F);  // xor 16
   return v;
 }
 
@@ -306,14 +313,15 @@ template <int D> __device__ __forceinline__ uint32_t xor_lane(uint32_t v) {
 // rotate and a bit-field merge.
 template <int BITS, int NW>
 __device__ __forceinline__ void transpose_codes(uint32_t (&w)[NW], int lane) {
-  constexpr int STEPS = BITS == 2 ? 4 : 3;
-  constexpr uint32_t kKeep[4] = {BITS == 2 ? 0x33333333u : 0x0F0F0F0Fu, BITS == 2 ? 0x0F0F0F0Fu : 0x00FF00FFu,
-                                 BITS == 2 ? 0x00FF00FFu : 0x0000FFFFu, 0x0000FFFFu};
+  constexpr int LOG_BITS = BITS == 1 ? 0 : (BITS == 2 ? 1 : 2);
+  constexpr int STEPS = 5 - LOG_BITS;
+  // step st swaps blocks of BITS * 2^st bits
+  constexpr uint32_t kKeep[5] = {0x55555555u, 0x33333333u, 0x0F0F0F0Fu, 0x00FF00FFu, 0x0000FFFFu};
 #pragma unroll
   for (int st = 0; st < STEPS; ++st) {
     const int d = 1 << st;
     const bool upper = (lane >> st) & 1;
-    const uint32_t keep = upper ? ~kKeep[st] : kKeep[st];
+    const uint32_t keep = upper ? ~kKeep[st + LOG_BITS] : kKeep[st + LOG_BITS];
     const uint32_t amt = upper ? (uint32_t)(BITS * d) : (uint32_t)(32 - BITS * d);
 #pragma unroll
     for (int k = 0; k < NW; ++k) {
@@ -322,7 +330,8 @@ __device__ __forceinline__ void transpose_codes(uint32_t (&w)[NW], int lane) {
         case 0: pv = xor_lane<1>(w[k]); break;
         case 1: pv = xor_lane<2>(w[k]); break;
         case 2: pv = xor_lane<4>(w[k]); break;
-        default: pv = xor_lane<8>(w[k]); break;
+        case 3: pv = xor_lane<8>(w[k]); break;
+        default: pv = xor_lane<16>(w[k]); break;
       }
       const uint32_t rot = __builtin_amdgcn_alignbit(pv, pv, amt);
       w[k] = (w[k] & keep) | (rot & ~keep);
@@ -420,9 +429,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void a
       pack_codes<4, 2>(x, g, w);
       if (valid) *reinterpret_cast<u32x4*>(blk + o * 32 + 16 * hh) = u32x4{w[0], w[1], w[2], w[3]};
     } else if (THREE && p.bits_k == 3) {
-      uint32_t w[4], hb[2], wh[2];
-      split_codes3(x, g, w, hb);
-      key_high_words(hb, wh);
+      uint32_t w[4], wh[2];
+      split_codes3_key(x, g, w, wh);
       if (valid) {
         *reinterpret_cast<u32x4*>(blk + o * 32 + 16 * hh) = u32x4{w[0], w[1], w[2], w[3]};
         *reinterpret_cast<u32x2*>(blk + kLowPlaneBytes + o * 16 + 8 * hh) = u32x2{wh[0], wh[1]};
@@ -483,19 +491,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void a
       uint32_t* dst = words + (o0 / 16 + g16) * kHeadDim + 64 * hh + r;
 #pragma unroll
       for (int k = 0; k < 4; ++k) dst[16 * k] = w[k];
-      // high plane: one word per channel holds the wave's 32 tokens.  The ballot of channel
-      // j's bit gives token tl at bit tl (lanes 0-31: channel j, lanes 32-63: channel 64 + j);
-      // lane j keeps both words, and a byte permute moves token t to value_hi_bit(t)
-      uint32_t h0 = 0u, h1 = 0u;
-#pragma unroll
-      for (int j = 0; j < 64; ++j) {
-        const uint64_t bal = __ballot((hb[j / 32] >> (j % 32)) & 1u);
-        h0 = lane == j ? (uint32_t)bal : h0;
-        h1 = lane == j ? (uint32_t)(bal >> 32) : h1;
-      }
-      uint32_t* hw = words + kLowPlaneBytes / 4 + (o0 / 32) * kHeadDim;
-      hw[lane] = __builtin_amdgcn_perm(h0, h0, 0x03010200u);
-      hw[64 + lane] = __builtin_amdgcn_perm(h1, h1, 0x03010200u);
+      // high plane: one word per channel holds the wave's 32 tokens.  A 32 x 32 bit
+      // transpose over the lanes of each half turns lane tl's bits of channels 64hh + 32k + j
+      // into lane tl's word k = channel 64hh + 32k + tl with token t at bit t; a byte permute
+      // moves token t to value_hi_bit(t)
+      transpose_codes<1, 2>(hb, lane);
+      uint32_t* hw = words + kLowPlaneBytes / 4 + (o0 / 32) * kHeadDim + 64 * hh + tl;
+      hw[0] = __builtin_amdgcn_perm(hb[0], hb[0], 0x03010200u);
+      hw[32] = __builtin_amdgcn_perm(hb[1], hb[1], 0x03010200u);
     } else {
       uint32_t w[8];
       pack_codes<8, 4>(x, g, w);

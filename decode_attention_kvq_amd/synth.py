@@ -83,6 +83,11 @@ WORKLOADS = {
                                    "percentile", "bf16", True),
     "long-b16-128k-quest": Workload("long-b16-128k-quest", 4, 64, 8, 16, 131072, 2, 2, "rms",
                                     "bf16", True),
+    # 3-bit codes (two bit planes) on the batch-64 and prefill shapes
+    "qwen3-8b-b64-16k-3bit": Workload("qwen3-8b-b64-16k-3bit", 2, 32, 8, 64, 16384, 3, 3, "percentile",
+                                      "bf16", True),
+    "prefill-8x32k-3bit": Workload("prefill-8x32k-3bit", 3, 8, 8, 1, 32768, 3, 3,
+                                   "percentile", "bf16", True),
 }
 
 
