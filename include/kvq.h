@@ -24,7 +24,7 @@
  *   - Arguments are validated on the host before anything is enqueued; a non-OK status
  *     means nothing was enqueued.  kvq_last_error() then returns a message for the
  *     calling thread.
- *   - Shapes are fixed by the layout: head_dim 128, page_size 64 tokens, 2- or 4-bit
+ *   - Shapes are fixed by the layout: head_dim 128, page_size 64 tokens, 2-, 3- or 4-bit
  *     codes.  Other values return KVQ_ERR_UNSUPPORTED.
  *   - Floating-point inputs must be finite.
  *
@@ -38,8 +38,15 @@
  *                   consecutive tokens of one channel c)
  *   scales  64 fp16 (token o at byte 2*o of this section)
  *   zeros   64 fp16 (token o at byte 2*o of this section)
+ * 3-bit codes ("WUSH-KV" §5.1 evaluates 2, 3 and 4 bits) are two bit planes in the
+ * 3072-byte code section: bytes 0..2047 hold bits 0-1 of every code laid out exactly as
+ * a 2-bit code section; bytes 2048..3071 (words 512..767) hold bit 2:
+ *           keys:   word 512 + o*4 + c/32, channel offset u = c%32 at bit
+ *                   4*((u%16)/2) + 2*(u/16) + u%2
+ *           values: word 512 + (o/32)*128 + c, token offset t = o%32 at bit
+ *                   t%8 + 16*((t/8)%2) + 8*(t/16)
  * A dequantized element is fma(code, scale, zero) in fp32.  2-bit blocks are 2304 bytes
- * (2.25 bits per element), 4-bit blocks 4352 bytes (4.25 bits per element).
+ * (2.25 bits per element), 3-bit blocks 3328 bytes (3.25), 4-bit blocks 4352 bytes (4.25).
  *
  * Quantizer of one group x[0..127] (one token of one KV head):
  *   percentile: lo, hi = linear-interpolated order statistics at p_lo, p_hi
@@ -82,8 +89,8 @@ typedef struct kvq_cache_desc {
   int32_t num_kv_heads;   /* >= 1 */
   int32_t head_dim;       /* must be 128 */
   int32_t page_size;      /* must be 64 */
-  int32_t bits_k;         /* 2 or 4 */
-  int32_t bits_v;         /* 2 or 4 */
+  int32_t bits_k;         /* 2, 3 or 4 */
+  int32_t bits_v;         /* 2, 3 or 4 */
   int32_t quant_k;        /* kvq_quantizer for keys */
   int32_t quant_v;        /* kvq_quantizer for values */
   float p_lo, p_hi;       /* percentile quantizer: 0 <= p_lo <= p_hi <= 1 */
@@ -93,7 +100,7 @@ typedef struct kvq_cache_desc {
   void* v_pages;          /* device, [num_pages][num_kv_heads][kvq_block_bytes(bits_v)] */
 } kvq_cache_desc;
 
-/* Bytes of one (page, KV head) block for 2- or 4-bit codes; 0 for other widths. */
+/* Bytes of one (page, KV head) block for 2-, 3- or 4-bit codes; 0 for other widths. */
 size_t kvq_block_bytes(int32_t bits);
 
 /* Write path: transform, clip, quantize and pack n_tokens new tokens.
