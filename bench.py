@@ -14,7 +14,9 @@ tokens read per second (batch x context per step time).  `roofline` is for the s
 dominant kernel, the decode: algorithmic bytes per launch over its average launch time
 (HIP events on the launch stream around the timed replay of a decode-only graph) against
 8 TB/s.  `cpu_baseline` is the CPU oracle's decode timed on a bounded sample of sequences
-of the same shape.
+of the same shape.  `step_ms_p10_p50_p90` spreads nine more replays of the timed graph;
+`reference_bandwidth` is what plain torch kernels reach on the same GPU (a 1 GiB read and
+a 1 GiB copy), for context.
 """
 from __future__ import annotations
 
@@ -36,7 +38,9 @@ def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    # 400 warm-up steps (~50 ms of back-to-back work): after idle the GPU runs the first
+    # milliseconds of a step stream ~15% slower until its clocks settle
+    ap.add_argument("--warmup", type=int, default=400)
     ap.add_argument("--workload", default="qwen3-8b-b64-16k")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
@@ -119,16 +123,39 @@ def time_steps(w, s, torch, api, steps, warmup):
 
     step()                                   # first call (library load) outside the graphs
     torch.cuda.synchronize()
-    ms_step, wall_step = graph_time(torch, step, steps, warmup)
+    ms_step, wall_step, more = graph_time(torch, step, steps, warmup, extra_replays=9)
     ms_app, _ = graph_time(torch, append, steps, warmup)
     ms_dec, _ = graph_time(torch, decode, steps, warmup)
-    return dict(step=ms_step, wall=wall_step, append=ms_app, decode=ms_dec)
+    return dict(step=ms_step, wall=wall_step, append=ms_app, decode=ms_dec, step_replays=[ms_step] + more)
 
 
-def graph_time(torch, fn, steps, warmup):
+def reference_bandwidth(torch, dev, nbytes=1 << 30, reps=10):
+    """What plain torch kernels reach on this GPU, as an achievable-bandwidth reference: the
+    sum of a 1 GiB fp32 tensor (read) and a 1 GiB device copy (read + write), in GB/s."""
+    src = torch.ones(nbytes // 4, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    out = {}
+    for name, fn, moved in (("read_sum", lambda: src.sum(), nbytes), ("copy", lambda: dst.copy_(src), 2 * nbytes)):
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        out[name + "_GB_s"] = moved / (e0.elapsed_time(e1) / reps * 1e-3) / 1e9
+    del src, dst
+    torch.cuda.empty_cache()
+    return out
+
+
+def graph_time(torch, fn, steps, warmup, extra_replays=0):
     """ms per call of fn: one replay of a HIP graph of `steps` calls (captured from the
     library calls on torch's current stream) after one replay of a graph of `warmup`
-    calls, bracketed by HIP events on the launch stream; also the host wall time."""
+    calls, bracketed by HIP events on the launch stream; also the host wall time.  With
+    extra_replays, the timed graph is replayed that many more times and the per-call times
+    of those replays are returned too."""
 
     def capture(count):
         g = torch.cuda.CUDAGraph()
@@ -149,8 +176,15 @@ def graph_time(torch, fn, steps, warmup):
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / steps
     wall = (time.perf_counter() - t0) * 1e3 / steps
+    more = []
+    for _ in range(extra_replays):
+        e0.record()
+        gt.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        more.append(e0.elapsed_time(e1) / steps)
     del gw, gt
-    return ms, wall
+    return (ms, wall, more) if extra_replays else (ms, wall)
 
 
 WINDOW = (32, 64, 64)          # S_sink, S_keep, S_flush: at most 159 full-precision positions
@@ -306,6 +340,7 @@ def main():
                      "kernel": "decode_kernel (kvq_decode_attn)", "algorithmic_bytes": dbytes,
                      "avg_us": t["decode"] * 1e3},
         "wall_ms_per_step": t["wall"],
+        "step_ms_p10_p50_p90": [float(np.percentile(t["step_replays"], q)) for q in (10, 50, 90)],
         "append_us": t["append"] * 1e3,
         "decode_us": t["decode"] * 1e3,
         "decode_tokens_per_s": cached / (t["decode"] * 1e-3),
@@ -314,6 +349,7 @@ def main():
         extra = {w.name + "-window": time_window(w, s, torch, api, args.steps, args.warmup)}
     del s
     torch.cuda.empty_cache()
+    rec["reference_bandwidth"] = reference_bandwidth(torch, dev)
     if args.extra:
         for name in ("qwen3-8b-b1-16k", "long-b16-128k-quest", "qwen3-8b-b64-16k-3bit"):
             w2 = synth.WORKLOADS[name]
