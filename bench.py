@@ -45,6 +45,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--extra", action="store_true", help="also time the other workloads")
+    ap.add_argument("--prefill-only", metavar="WORKLOAD", default=None,
+                    help="only time the bulk quantize-append of a prefill workload (for profiling)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run a plain device copy of BYTES bytes 5 times (the reference kernel "
                          "whose FETCH_SIZE/WRITE_SIZE readings scale the decode kernel's counters)")
@@ -317,6 +319,9 @@ def main():
     if not os.path.exists(os.path.join(ROOT, "decode_attention_kvq_amd", "libkvq.so")):
         kbuild.build()
     dev = torch.device("cuda:0")
+    if args.prefill_only:
+        print(json.dumps(time_prefill(synth.WORKLOADS[args.prefill_only], torch, api, calib, synth, dev)), flush=True)
+        return
     w = synth.WORKLOADS[args.workload]
     s = setup_decode(w, torch, api, calib, synth, dev)
     t = time_steps(w, s, torch, api, args.steps, args.warmup)
