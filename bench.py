@@ -359,7 +359,7 @@ def main():
         for name in ("qwen3-8b-b1-16k", "long-b16-128k-quest", "qwen3-8b-b64-16k-3bit"):
             w2 = synth.WORKLOADS[name]
             s2 = setup_decode(w2, torch, api, calib, synth, dev)
-            t2 = time_steps(w2, s2, torch, api, 20, 10)
+            t2 = time_steps(w2, s2, torch, api, 20, args.warmup)
             dby = decode_algorithmic_bytes(w2, w2.batch, w2.seq_len)
             extra[name] = {"step_us": t2["step"] * 1e3, "tokens_per_s": w2.batch * w2.seq_len / (t2["step"] * 1e-3),
                            "append_us": t2["append"] * 1e3, "decode_us": t2["decode"] * 1e3,
