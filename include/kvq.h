@@ -199,7 +199,7 @@ kvq_status kvq_dequant(const kvq_cache_desc* cache, int32_t which, const int64_t
  * Window tensors (k_win, v_win): device, [num_rows][sink + keep + flush][num_kv_heads][128]
  * of `dtype`, caller-owned.  Sequence b uses row win_rows[b] (row b when win_rows is NULL;
  * a row outside [0, num_rows) gives it no full-precision positions and nothing is written
- * there).  Position p < sink is slot p; a later position p is slot
+ * there).  The sequences of one call must use distinct rows (a decode step writes them).  Position p < sink is slot p; a later position p is slot
  * sink + (p - sink) % (keep + flush).  Keys are stored as given (post-RoPE, before the key
  * transform), so their scores use the plain query; values in the folded basis as given.
  * Queries, new keys and values, prompts and T_K are all of `dtype`.
