@@ -136,8 +136,8 @@ size_t kvq_decode_workspace_bytes(const kvq_cache_desc* cache, int32_t batch,
  *                last page are not read; a page id outside [0, num_pages) contributes
  *                nothing (its tokens are skipped).
  *   seq_lens     device, [batch] int32, 0 <= seq_lens[b] <= max_seq_len <= 64*max_pages
- *                (max_seq_len sizes the split; a larger seq_lens[b] is clamped to
- *                64*max_pages).
+ *                (max_seq_len sizes the split over workgroups: a seq_lens[b] above it is
+ *                not fully read; reads never go past 64*max_pages positions).
  *   sm_scale     softmax scale (1/sqrt(128) for standard attention).
  *   out          device, [batch][num_q_heads][128] fp32, in the transformed value basis;
  *                an empty sequence gives zeros.
