@@ -59,7 +59,7 @@ def _setup(rng, B, H, G, lens, bits, quant, dtype, transform, config=1):
 
 
 def _gpu(s, H, bits, quant, dtype, lens, fused=True):
-    tdt = {"bf16": torch.bfloat16, "f32": torch.float32}[dtype]
+    tdt = {"bf16": torch.bfloat16, "f16": torch.float16, "f32": torch.float32}[dtype]
     cache = api.KVCache(s["P"], H, bits[0], bits[1], quant[0], quant[1],
                         k_pages=torch.from_numpy(s["kp"].copy()).cuda(),
                         v_pages=torch.from_numpy(s["vp"].copy()).cuda())
@@ -87,6 +87,8 @@ CASES = [
     (2, 1, 8, [4097, 3000], (2, 4), ("percentile", "rms"), "f32", False),
     (1, 2, 4, [9000], (2, 2), ("percentile", "percentile"), "bf16", True),      # split over chunks
     (5, 1, 1, [300, 64, 128, 1, 2], (4, 4), ("percentile", "percentile"), "f32", True),
+    (3, 2, 4, [33, 64, 1500], (3, 3), ("percentile", "percentile"), "bf16", True),
+    (2, 2, 8, [700, 96], (3, 2), ("rms", "rms"), "f16", False),
 ]
 
 
