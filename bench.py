@@ -233,14 +233,17 @@ def time_window(w, s, torch, api, steps, warmup):
             "tokens_per_s": B * w.seq_len / (amort * 1e-3)}
 
 
-def time_prefill(w, torch, api, calib, synth, dev, reps=20):
+def time_prefill(w, torch, api, calib, synth, dev, reps=200, warmup=1000):
+    """Steady-state time of one bulk append (HIP events around `reps` back-to-back
+    launches after `warmup` untimed ones: ~40 ms of warm-up, like the decode's, so that
+    the clocks have settled)."""
     n, H = w.seq_len, w.heads_kv
     cache = api.KVCache(n // 64, H, w.bits_k, w.bits_v, device=dev)
     k, v = synth.kv_tokens_torch(w, n, dev)
     ts = [calib.calibrate_key_transform(*synth.calibration_set(w.config, h, 4))[0] for h in range(H)]
     t_k = torch.from_numpy(np.stack(ts)).to(torch.bfloat16).to(dev)
     slots = torch.arange(n, dtype=torch.int64, device=dev)
-    for _ in range(3):
+    for _ in range(warmup):
         api.kvq_quantize_append(cache, k, v, slots, t_k=t_k)
     torch.cuda.synchronize()
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]

@@ -24,12 +24,12 @@ COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
           "-I", os.path.join(ROOT, "include"), "-I", CSRC]
 
 
-# The read path has no NaN semantics to honour (absent tokens are masked by selects), so
-# max/min need no canonicalisation; the write path keeps strict IEEE behaviour.
+# Neither path has NaN semantics to honour (absent tokens are masked by selects; the write
+# path's inputs must be finite), so min/max/med3 need no canonicalisation of their operands.
 # Matrix-core accumulators stay in ordinary VGPRs (no copies through AGPRs; the write
 # path's transform results are then its working registers).
 EXTRA = {"kvq_decode.hip": ["-fno-honor-nans", "-mllvm", "-amdgpu-mfma-vgpr-form"],
-         "kvq_append.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+         "kvq_append.hip": ["-fno-honor-nans", "-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def _compile(src: str) -> str:

@@ -24,7 +24,7 @@
 //     K smallest/largest use a 128-element bitonic sort across the wavefront.
 //   * rms clip: in-lane pairwise tree over the half, one exchange, correctly rounded
 //     sqrt.
-//   * codes: rint by the fp32 addition of 2^23, packed by shifted integer sums.
+//   * codes: rounded and packed a byte at a time by v_cvt_pk_u8_f32, bytes merged by shifts.
 //   * keys: each lane writes its half of the token's row (16 or 32 bytes).
 //   * values: codes are transposed through LDS; when the wave's 32 tokens fill an
 //     aligned run of one page, whole words are stored; otherwise the wave merges one
@@ -146,22 +146,49 @@ __device__ __forceinline__ void transform_f32(const float* tok_row, const float*
   }
 }
 
+// Inserts v into the sorted K smallest (lo) and K largest (hi) values seen so far.
+template <int K>
+__device__ __forceinline__ void insert_extreme(float v, float w, float (&lo)[K], float (&hi)[K]) {
+#pragma unroll
+  for (int k = K - 1; k >= 1; --k) {
+    lo[k] = __builtin_amdgcn_fmed3f(lo[k - 1], lo[k], v);
+    hi[k] = __builtin_amdgcn_fmed3f(hi[k - 1], hi[k], w);
+  }
+  lo[0] = fminf(lo[0], v);
+  hi[0] = fmaxf(hi[0], w);
+}
+
 // Smallest / largest K values of the token's 128 (lane + partner lane), sorted:
 // lo[k] = s[k], hi[k] = s[127-k].
 template <int K>
 __device__ __forceinline__ void select_extremes(const float (&x)[64], float (&lo)[K], float (&hi)[K]) {
 #pragma unroll
   for (int k = 0; k < K; ++k) { lo[k] = __builtin_inff(); hi[k] = -__builtin_inff(); }
+  if constexpr (K == 3) {
+    // The lane's values in triples, each sorted by one min3, med3 and max3.  A value among
+    // the 3 smallest is either the minimum of its triple and among the 3 smallest triple
+    // minima, or the smallest triple median (a smaller median would bring its own minimum:
+    // 3 smaller values), or the smallest triple maximum (its two triple-mates are smaller,
+    // so nothing else is).  Mirrored for the 3 largest.  13 operations per triple instead
+    // of 18 for inserting each value.
+    float lmed = __builtin_inff(), lmax = __builtin_inff(), hmed = -__builtin_inff(), hmin = -__builtin_inff();
 #pragma unroll
-  for (int m = 0; m < 64; ++m) {
-    const float v = x[m];
-#pragma unroll
-    for (int k = K - 1; k >= 1; --k) {
-      lo[k] = __builtin_amdgcn_fmed3f(lo[k - 1], lo[k], v);
-      hi[k] = __builtin_amdgcn_fmed3f(hi[k - 1], hi[k], v);
+    for (int m = 0; m + 3 <= 64; m += 3) {
+      const float a = x[m], b = x[m + 1], c = x[m + 2];
+      const float mn = fminf(fminf(a, b), c), md = __builtin_amdgcn_fmed3f(a, b, c);
+      const float mx = fmaxf(fmaxf(a, b), c);
+      insert_extreme<K>(mn, mx, lo, hi);
+      lmed = fminf(lmed, md);
+      lmax = fminf(lmax, mx);
+      hmed = fmaxf(hmed, md);
+      hmin = fmaxf(hmin, mn);
     }
-    lo[0] = fminf(lo[0], v);
-    hi[0] = fmaxf(hi[0], v);
+    insert_extreme<K>(x[63], x[63], lo, hi);
+    insert_extreme<K>(lmed, hmed, lo, hi);
+    insert_extreme<K>(lmax, hmin, lo, hi);
+  } else {
+#pragma unroll
+    for (int m = 0; m < 64; ++m) insert_extreme<K>(x[m], x[m], lo, hi);
   }
   float plo[K], phi[K];
 #pragma unroll
@@ -238,24 +265,25 @@ __device__ __forceinline__ void clip_bounds(const float (&x)[64], int quant, flo
 }
 
 // Codes of a lane's values, packed R = 32/bits to a word (value m at bits bits*(m % R) of
-// word m / R).  rint of t in [0, L] is taken by the fp32 addition of 2^23 (round to nearest
-// even, exact), whose bit pattern is 0x4B000000 + code; the words are summed shifted and the
-// constant sum of the 0x4B000000 terms is removed once per word.
+// word m / R).  The clamped t in [0, L] goes through v_cvt_pk_u8_f32, which rounds to the
+// nearest integer with ties to even (checked for every fp32 value in [0, 256)) and writes
+// one byte of a word: byte-word s gets the codes of values i * R/4 + s (i = 0..3) in its
+// bytes, and shifting it by bits * s before merging puts value e at bits bits * e.
 template <int NW, int BITS>
 __device__ __forceinline__ void pack_codes(const float* x, const GroupQuant& g, uint32_t (&w)[NW]) {
-  constexpr int R = 32 / BITS;
-  constexpr uint32_t kMagic = 0x4B000000u;
-  uint32_t junk = 0;
-#pragma unroll
-  for (int e = 0; e < R; ++e) junk += kMagic << (BITS * e);
+  constexpr int R = 32 / BITS, S = R / 4;
 #pragma unroll
   for (int q = 0; q < NW; ++q) {
-    uint32_t acc = 0u - junk;
+    uint32_t acc = 0u;
 #pragma unroll
-    for (int e = 0; e < R; ++e) {
-      const float t = code_arg(x[R * q + e], g);
-      const float c = __builtin_amdgcn_fmed3f(t, 0.0f, g.lmax) + 8388608.0f;
-      acc += __float_as_uint(c) << (BITS * e);
+    for (int s = 0; s < S; ++s) {
+      uint32_t b = 0u;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float c = __builtin_amdgcn_fmed3f(code_arg(x[R * q + i * S + s], g), 0.0f, g.lmax);
+        b = __builtin_amdgcn_cvt_pk_u8_f32(c, (unsigned)i, b);
+      }
+      acc = s == 0 ? b : (acc | (b << (BITS * s)));
     }
     w[q] = acc;
   }

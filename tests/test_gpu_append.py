@@ -23,9 +23,18 @@ pytestmark = pytest.mark.gpu
 QMAP = {"percentile": oracle.PERCENTILE, "rms": oracle.RMS}
 
 
+def _tie_row(levels):
+    """A group whose 1%/99% clip bounds are exactly 0 and L (three of each), so the scale is
+    1 and every other value k + 1/2 lands exactly halfway between two codes: the rounding
+    must go to the even code."""
+    mids = [k + 0.5 for k in range(levels)]
+    row = [0.0] * 3 + [float(levels)] * 3 + [mids[i % levels] for i in range(122)]
+    return np.array(row, dtype=np.float32)
+
+
 def _special_rows(x, rng):
-    """Overwrite some token rows with edge cases: constant, zeros, +-0, ties, heavy tails,
-    tiny and huge magnitudes."""
+    """Overwrite some token rows with edge cases: constant, zeros, +-0, integers, heavy
+    tails, tiny and huge magnitudes, and exact rounding ties at 2, 3 and 4 bits."""
     n = x.shape[0]
     if n > 8:
         x[1] = 0.37
@@ -35,6 +44,10 @@ def _special_rows(x, rng):
         x[5] = rng.standard_t(1.5, size=x[5].shape)
         x[6] *= 1e-6
         x[7] *= 300.0
+    if n > 11:
+        x[8] = _tie_row(3)
+        x[9] = _tie_row(7)
+        x[10] = _tie_row(15)
     return x
 
 
