@@ -41,6 +41,10 @@ constexpr int kTileTokens = 32;
 constexpr int kWavesPerBlock = 4;
 constexpr int kBlockTokens = kTileTokens * kWavesPerBlock;
 constexpr int kTtStride = 136;   // padded LDS row of T^T (elements): spreads banks
+// T^T row j keeps its 16-byte group g at group g ^ tt_swizzle(j): with the padding, the
+// matrix-core operand reads stay at two lanes per bank and the staging writes (16 rows 4
+// apart per instruction) drop from eight to two.
+__device__ __forceinline__ int tt_swizzle(int j) { return (j >> 3) & 7; }
 
 template <typename T> struct Mfma;
 template <> struct Mfma<__bf16> {
@@ -117,7 +121,8 @@ __device__ __forceinline__ void transform_mfma(const u32x4 (&kop)[8], const uint
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) {
       const int ch = 64 * ((rho >> 2) & 1) + 16 * mt + 4 * (rho >> 3) + (rho & 3);
-      u32x4 araw = *reinterpret_cast<const u32x4*>(tt + ch * kTtStride + 16 * ks + 8 * kk);
+      const int grp = (2 * ks + kk) ^ tt_swizzle(ch);
+      u32x4 araw = *reinterpret_cast<const u32x4*>(tt + ch * kTtStride + 8 * grp);
       acc[mt] = Mfma<TIn>::mma(__builtin_bit_cast(vec, araw), b, acc[mt]);
     }
   }
@@ -406,7 +411,19 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void a
     // ---------------- keys ----------------
     uint16_t* tt = reinterpret_cast<uint16_t*>(lds);
     if constexpr (kMfmaType) {
-      // the row loads go out first, then this thread's share of T
+      // This thread's share of T goes out first, then the row loads: loads complete in
+      // order, so T^T is staged (and the barrier passed) while the rows are still in flight.
+      // Wave w reads rows 32w .. 32w + 31 of T, 8 half rows (1 KB, whole cache lines) per
+      // load: load i gives lane l the 8 elements from column 64 (i % 2) + 8 (l % 8) of row
+      // 32w + 8 (i / 2) + l / 8.
+      const TIn* th = reinterpret_cast<const TIn*>(p.t) + (int64_t)h * kHeadDim * kHeadDim;
+      u32x4 tl[8];
+      if (p.t != nullptr) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+          tl[i] = *reinterpret_cast<const u32x4*>(th + (32 * wave + 8 * (i >> 1) + (lane >> 3)) * kHeadDim +
+                                                  64 * (i & 1) + 8 * (lane & 7));
+      }
       u32x4 kraw[8];
 #pragma unroll
       for (int q = 0; q < 8; ++q) {
@@ -415,27 +432,26 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void a
         kraw[q] = *reinterpret_cast<const u32x4*>(row + koff);
       }
       if (p.t != nullptr) {
-        const TIn* th = reinterpret_cast<const TIn*>(p.t) + (int64_t)h * kHeadDim * kHeadDim;
-        // T^T into LDS without bank conflicts: wave w, unit u covers rows j0 = 8 (w + 4u)
-        // .. j0 + 7 of T^T; lane l reads T[2l][j0..j0+7] and T[2l+1][j0..j0+7] and writes,
-        // per row, the dword holding columns 2l and 2l+1, so each store is one contiguous
-        // row segment of the wave.
-        u32x4 ta[4], tb[4];
+        // Lanes l and l ^ 8 hold rows r and r + 1 (r even) at the same 8 columns; they swap
+        // halves so that the even lane has both rows at the first 4 columns and the odd lane
+        // at the last 4.  Each lane then writes, for 4 columns j, the dword (T[r][j],
+        // T[r+1][j]) of T^T row j.
+        const bool odd = (lane >> 3) & 1;
+        uint32_t* tt32 = reinterpret_cast<uint32_t*>(tt);
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const int j0 = 8 * (wave + 4 * u);
-          ta[u] = *reinterpret_cast<const u32x4*>(th + (2 * lane) * kHeadDim + j0);
-          tb[u] = *reinterpret_cast<const u32x4*>(th + (2 * lane + 1) * kHeadDim + j0);
-        }
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const int j0 = 8 * (wave + 4 * u);
-          uint32_t* trow = reinterpret_cast<uint32_t*>(tt + j0 * kTtStride) + lane;
+        for (int i = 0; i < 8; ++i) {
+          const uint32_t s0 = odd ? tl[i][0] : tl[i][2], s1 = odd ? tl[i][1] : tl[i][3];
+          const uint32_t r0 = xor_lane<8>(s0), r1 = xor_lane<8>(s1);
+          const uint32_t lo0 = odd ? r0 : tl[i][0], lo1 = odd ? r1 : tl[i][1];   // row r
+          const uint32_t hi0 = odd ? tl[i][2] : r0, hi1 = odd ? tl[i][3] : r1;   // row r + 1
+          const int c = 16 * wave + 4 * (i >> 1) + (lane >> 4);     // dword column r / 2
+          const int jb = 64 * (i & 1) + 8 * (lane & 7) + 4 * (int)odd;
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            // row j0+2e takes the low halves of T[2l] and T[2l+1], row j0+2e+1 the high
-            trow[(2 * e) * (kTtStride / 2)] = __builtin_amdgcn_perm(tb[u][e], ta[u][e], 0x05040100u);
-            trow[(2 * e + 1) * (kTtStride / 2)] = __builtin_amdgcn_perm(tb[u][e], ta[u][e], 0x07060302u);
+            const int j = jb + e;
+            const uint32_t lo = e < 2 ? lo0 : lo1, hi = e < 2 ? hi0 : hi1;
+            const uint32_t v = __builtin_amdgcn_perm(hi, lo, (e & 1) ? 0x07060302u : 0x05040100u);
+            tt32[j * (kTtStride / 2) + (((c >> 2) ^ tt_swizzle(j)) << 2) + (c & 3)] = v;
           }
         }
         __syncthreads();
