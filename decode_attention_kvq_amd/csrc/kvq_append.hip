@@ -436,23 +436,29 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void a
         // halves so that the even lane has both rows at the first 4 columns and the odd lane
         // at the last 4.  Each lane then writes, for 4 columns j, the dword (T[r][j],
         // T[r+1][j]) of T^T row j.
+        // The rows j = 64 (i % 2) + 8 m + 4 odd + e (m = l % 8) all have tt_swizzle(j) = m.
         const bool odd = (lane >> 3) & 1;
-        uint32_t* tt32 = reinterpret_cast<uint32_t*>(tt);
+        const int m = lane & 7;
+        const uint32_t keep = odd ? ~0u : 0u;
+        // byte selectors: the low half from row r, the high half from row r + 1, whichever
+        // operand holds them (own dword for row r on even lanes, for row r + 1 on odd ones)
+        const uint32_t sel_lo = odd ? 0x01000504u : 0x05040100u;
+        const uint32_t sel_hi = odd ? 0x03020706u : 0x07060302u;
+        uint32_t* tt32 = reinterpret_cast<uint32_t*>(tt) + (8 * m + 4 * (int)odd) * (kTtStride / 2) + (lane >> 4);
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-          const uint32_t s0 = odd ? tl[i][0] : tl[i][2], s1 = odd ? tl[i][1] : tl[i][3];
-          const uint32_t r0 = xor_lane<8>(s0), r1 = xor_lane<8>(s1);
-          const uint32_t lo0 = odd ? r0 : tl[i][0], lo1 = odd ? r1 : tl[i][1];   // row r
-          const uint32_t hi0 = odd ? tl[i][2] : r0, hi1 = odd ? tl[i][3] : r1;   // row r + 1
-          const int c = 16 * wave + 4 * (i >> 1) + (lane >> 4);     // dword column r / 2
-          const int jb = 64 * (i & 1) + 8 * (lane & 7) + 4 * (int)odd;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int j = jb + e;
-            const uint32_t lo = e < 2 ? lo0 : lo1, hi = e < 2 ? hi0 : hi1;
-            const uint32_t v = __builtin_amdgcn_perm(hi, lo, (e & 1) ? 0x07060302u : 0x05040100u);
-            tt32[j * (kTtStride / 2) + (((c >> 2) ^ tt_swizzle(j)) << 2) + (c & 3)] = v;
-          }
+          // own dwords for the lane's 4 columns; the partner gets the other two
+          const uint32_t own0 = (keep & tl[i][2]) | (~keep & tl[i][0]);
+          const uint32_t own1 = (keep & tl[i][3]) | (~keep & tl[i][1]);
+          const uint32_t snd0 = (keep & tl[i][0]) | (~keep & tl[i][2]);
+          const uint32_t snd1 = (keep & tl[i][1]) | (~keep & tl[i][3]);
+          const uint32_t got0 = xor_lane<8>(snd0), got1 = xor_lane<8>(snd1);
+          const int grp = (4 * wave + (i >> 1)) ^ m;                // swizzled 16-byte group
+          uint32_t* dst = tt32 + 64 * (i & 1) * (kTtStride / 2) + 4 * grp;
+          dst[0 * (kTtStride / 2)] = __builtin_amdgcn_perm(got0, own0, sel_lo);
+          dst[1 * (kTtStride / 2)] = __builtin_amdgcn_perm(got0, own0, sel_hi);
+          dst[2 * (kTtStride / 2)] = __builtin_amdgcn_perm(got1, own1, sel_lo);
+          dst[3 * (kTtStride / 2)] = __builtin_amdgcn_perm(got1, own1, sel_hi);
         }
         __syncthreads();
         transform_mfma<TIn>(kraw, tt, lane, x);
