@@ -131,6 +131,31 @@ def time_steps(w, s, torch, api, steps, warmup):
     return dict(step=ms_step, wall=wall_step, append=ms_app, decode=ms_dec, step_replays=[ms_step] + more)
 
 
+def time_decode_from_hbm(w, s, torch, api, steps, warmup):
+    """The decode alone over copies of the cache that together exceed the MALL twice over,
+    one copy per call in turn (each with its own block table), so that every call reads its
+    pages from HBM.  For caches that fit the MALL (batch 1).  Returns ms per call."""
+    copies = max(2, -(-2 * MALL_BYTES // max(1, s["cache"].k_pages.numel() + s["cache"].v_pages.numel())) + 1)
+    src = s["cache"]
+    big = api.KVCache(src.num_pages * copies, src.num_kv_heads, src.bits_k, src.bits_v, src.quant_k,
+                      src.quant_v, src.p_lo, src.p_hi, src.alpha_k, src.alpha_v, device=src.k_pages.device)
+    for c in range(copies):
+        big.k_pages[c * src.num_pages:(c + 1) * src.num_pages].copy_(src.k_pages)
+        big.v_pages[c * src.num_pages:(c + 1) * src.num_pages].copy_(src.v_pages)
+    bts = [s["bt"] + c * src.num_pages for c in range(copies)]
+    state = {"i": 0}
+
+    def decode():
+        bt = bts[state["i"] % copies]
+        state["i"] += 1
+        api.kvq_decode_attn(big, s["q"], bt, s["seq"], w.seq_len, t_k_inv_t=s["t_inv"], out=s["out"],
+                            workspace=s["ws"])
+
+    ms, _ = graph_time(torch, decode, max(steps, copies), max(warmup, copies))
+    del big, bts
+    return ms, copies
+
+
 def reference_bandwidth(torch, dev, nbytes=1 << 30, reps=10):
     """What plain torch kernels reach on this GPU, as an achievable-bandwidth reference: the
     sum of a 1 GiB fp32 tensor (read) and a 1 GiB device copy (read + write), in GB/s."""
@@ -402,6 +427,10 @@ def main():
                            "append_us": t2["append"] * 1e3, "decode_us": t2["decode"] * 1e3,
                            "decode_GB_s": dby / (t2["decode"] * 1e-3) / 1e9,
                            "decode_frac": dby / (t2["decode"] * 1e-3) / HBM_PEAK}
+            if dby < MALL_BYTES:
+                # the cache fits the MALL: also the decode with every call reading from HBM
+                ms_h, copies = time_decode_from_hbm(w2, s2, torch, api, 20, args.warmup)
+                extra[name].update({"decode_us_from_hbm": ms_h * 1e3, "cache_copies": copies})
             del s2
             torch.cuda.empty_cache()
         for name in ("prefill-8x32k-4bit", "prefill-8x32k-2bit", "prefill-8x32k-3bit"):
