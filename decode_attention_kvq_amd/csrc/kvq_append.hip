@@ -17,19 +17,21 @@
 //   * transform (keys): D[out-channel][token] = T^T[out][in] . K^T[in][token] on the
 //     matrix cores (32x32x16, bf16 or f16, fp32 accumulate); the rows of T^T are permuted
 //     so that accumulator register r of M-tile mt on lane half hh is channel
-//     64*hh + 16*mt + r.  T^T is staged once per workgroup in LDS.
+//     64*hh + 16*mt + r.  T^T is staged once per workgroup in LDS from whole cache lines
+//     of T (lane pairs swap halves to form T^T dwords; 16-byte groups XOR-swizzled).
 //   * percentile clip: bottom-K / top-K insertion networks (v_med3) over the lane's
-//     64 values, one exchange with the partner lane, then the order statistics;
-//     order statistics do not depend on how they are found.  Positions outside the
-//     K smallest/largest use a 128-element bitonic sort across the wavefront.
+//     64 values (for K = 3 over sorted triples' candidates), one exchange with the
+//     partner lane, then the order statistics; order statistics do not depend on how
+//     they are found.  Positions outside the K smallest/largest use a 128-element
+//     bitonic sort across the wavefront.
 //   * rms clip: in-lane pairwise tree over the half, one exchange, correctly rounded
 //     sqrt.
 //   * codes: rounded and packed a byte at a time by v_cvt_pk_u8_f32, bytes merged by shifts.
 //   * keys: each lane writes its half of the token's row (16 or 32 bytes).
-//   * values: codes are transposed through LDS; when the wave's 32 tokens fill an
-//     aligned run of one page, whole words are stored; otherwise the wave merges one
-//     token at a time into its words with atomic AND/OR (contiguous words per
-//     instruction), so other tokens' bits survive.
+//   * values: when the wave's 32 tokens fill an aligned run of one page, the packed codes
+//     are transposed across lanes in registers and whole words are stored; otherwise the
+//     codes go through LDS as bytes and the wave merges one token at a time into its words
+//     with atomic AND/OR (contiguous words per instruction), so other tokens' bits survive.
 #include "kvq_device.h"
 #include "kvq_encode.h"
 #include "kvq_internal.h"
