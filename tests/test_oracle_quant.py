@@ -7,6 +7,7 @@ import numpy as np
 import pytest
 
 from decode_attention_kvq_amd import synth
+from helpers import rms_order_rows
 
 
 def _ulp(x):
@@ -72,6 +73,21 @@ def test_rms_clip_closed_form(orc):
     ref = alpha * np.sqrt(np.mean(x.astype(np.float64) ** 2, axis=1))
     assert np.all(np.abs(hi - ref) <= 4 * _ulp(ref) + 1e-30)
     assert np.array_equal(lo, -hi)
+
+
+def test_rms_sum_order_worked_rows(orc):
+    """The fixed summation order is visible in the clip bound: rms = sqrtf(sum / 128)
+    (correctly rounded) and the bound alpha * rms, both fp32, from the hand-worked sums."""
+    rows, sums = rms_order_rows()
+    alpha = np.float32(2.83)
+    _, _, _, lo, hi = orc.quantize_rows(rows, 2, orc.RMS, alpha=float(alpha))
+    want = alpha * np.sqrt(sums / np.float32(128.0))
+    assert want.dtype == np.float32
+    assert np.array_equal(hi, want), (hi, want)
+    assert np.array_equal(lo, -want)
+    # the other orders named above give other bounds for these rows
+    other = alpha * np.sqrt(np.array([2.0 ** 24 + 64, 2.0 ** 24 + 62], np.float32) / np.float32(128.0))
+    assert not np.any(hi == other)
 
 
 @pytest.mark.parametrize("bits", [2, 3, 4])
