@@ -24,8 +24,9 @@
 //     partner lane, then the order statistics; order statistics do not depend on how
 //     they are found.  Positions outside the K smallest/largest use a 128-element
 //     bitonic sort across the wavefront.
-//   * rms clip: in-lane pairwise tree over the half, one exchange, correctly rounded
-//     sqrt.
+//   * rms clip: the 128-channel pairwise tree whose first level (stride 64) pairs the two
+//     lanes of a token (one half-swap per two squares), the rest in-lane, then one
+//     exchange and a correctly rounded sqrt.
 //   * codes: rounded and packed a byte at a time by v_cvt_pk_u8_f32, bytes merged by shifts.
 //   * keys: each lane writes its half of the token's row (16 or 32 bytes).
 //   * values: when the wave's 32 tokens fill an aligned run of one page, the packed codes

@@ -37,17 +37,29 @@ __device__ __forceinline__ float interpolate(float s0, float s1, float f) {
   return __builtin_fmaf(f, s1 - s0, s0) + 0.0f;
 }
 
-// Sum of squares of the token's 128 values: each lane's half by a pairwise tree
-// (stride 32..1), then the two halves added.
+// Sum of squares of the token's 128 values in the encoder's order: one pairwise tree over
+// the channel index c (stride 64, 32, ..., 1: element c < stride adds element c + stride).
+// The lane holds channels 64*hh + m in x[m] and its partner lane (lane ^ 32) the other
+// half, so stride 64 adds the two lanes' m-th squares.  One half-swap of the squares of
+// m = 2j and 2j + 1 puts both partners' values of 2j in the low lanes and of 2j + 1 in the
+// high lanes, so each lane adds one of the two sums: t[j] is c = 2j (low lanes) or 2j + 1
+// (high lanes).  Strides 32 .. 2 then pair t[j] with t[j + 16 .. 1] in-lane, and stride 1
+// adds the partners' t[0].  Additions commute, so both lanes end with the same total.
 __device__ __forceinline__ float rms_bound(const float (&x)[64], float alpha) {
-  float sq[64];
+  float t[32];
 #pragma unroll
-  for (int m = 0; m < 64; ++m) sq[m] = x[m] * x[m];
+  for (int j = 0; j < 32; ++j) {
+    const float a = x[2 * j] * x[2 * j], b = x[2 * j + 1] * x[2 * j + 1];
+    // lanes 32..63 of a trade places with lanes 0..31 of b
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+    t[j] = __uint_as_float((uint32_t)r[0]) + __uint_as_float((uint32_t)r[1]);
+  }
 #pragma unroll
-  for (int stride = 32; stride >= 1; stride >>= 1)
+  for (int stride = 16; stride >= 1; stride >>= 1)
 #pragma unroll
-    for (int m = 0; m < stride; ++m) sq[m] = sq[m] + sq[m + stride];
-  const float total = sq[0] + __shfl_xor(sq[0], 32);
+    for (int j = 0; j < stride; ++j) t[j] = t[j] + t[j + stride];
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(t[0]), __float_as_uint(t[0]), false, false);
+  const float total = __uint_as_float((uint32_t)r[0]) + __uint_as_float((uint32_t)r[1]);
   const float rms = sqrtf(total / 128.0f);
   return alpha * rms;
 }
@@ -166,12 +178,14 @@ __device__ __forceinline__ void wave_extremes3(float a, float b, float (&lo)[3],
 }
 
 #pragma clang fp contract(off)
-// Sum of squares in the encoder's order: per 64-channel half a pairwise tree over the
-// channel index (stride 32 .. 1), then the halves added.  Channel 2l+e is (lane l, e), so
-// channel strides 32 .. 2 pair lanes m and m + 16 .. m + 1 (lane ^ 16 .. ^ 1 for the lanes
-// m < stride whose sums the tree keeps); additions commute, so each level adds the pair.
+// Sum of squares in the encoder's order: one pairwise tree over the channel index (stride
+// 64, 32, ..., 1).  Channel 2l+e is (lane l, e), so channel stride 64 pairs lanes l and
+// l + 32 (a half swap), strides 32 .. 2 pair lanes m and m + 16 .. m + 1 (lane ^ 16 .. ^ 1
+// for the lanes m < stride whose sums the tree keeps), and stride 1 adds a lane's two
+// values; additions commute, so each level adds the pair and every lane ends with the total.
 __device__ __forceinline__ float wave_rms_bound(float a, float b, float alpha) {
   float sa = a * a, sb = b * b, x0, x1, y0, y1;
+  pair_of<5>(sa, x0, x1); pair_of<5>(sb, y0, y1); sa = x0 + x1; sb = y0 + y1;     // 64
   pair_of<4>(sa, x0, x1); pair_of<4>(sb, y0, y1); sa = x0 + x1; sb = y0 + y1;     // 32
   pair_of<3>(sa, x0, x1); pair_of<3>(sb, y0, y1); sa = x0 + x1; sb = y0 + y1;     // 16
   x1 = __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(sa), (4 << 10) | 0x1F));
@@ -179,9 +193,7 @@ __device__ __forceinline__ float wave_rms_bound(float a, float b, float alpha) {
   sa = sa + x1; sb = sb + y1;                                                     // 8
   pair_of<1>(sa, x0, x1); pair_of<1>(sb, y0, y1); sa = x0 + x1; sb = y0 + y1;     // 4
   pair_of<0>(sa, x0, x1); pair_of<0>(sb, y0, y1); sa = x0 + x1; sb = y0 + y1;     // 2
-  sa = sa + sb;                                                                   // 1
-  pair_of<5>(sa, x0, x1);                                                         // halves
-  return alpha * sqrtf((x0 + x1) / 128.0f);
+  return alpha * sqrtf((sa + sb) / 128.0f);                                       // 1
 }
 #pragma clang fp contract(on)
 

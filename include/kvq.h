@@ -52,9 +52,9 @@
  *   percentile: lo, hi = linear-interpolated order statistics at p_lo, p_hi
  *               (rank p*127 formed in double, weight f rounded to float,
  *               v = fmaf(f, s[i+1] - s[i], s[i]) + 0.0f over the sorted values s)
- *   rms:        lo = -alpha*r, hi = +alpha*r, r = sqrtf(sum(x^2)/128) with the sum
- *               taken as two 64-element halves, each summed by a pairwise tree
- *               (stride 32, 16, ..., 1), then added
+ *   rms:        lo = -alpha*r, hi = +alpha*r, r = sqrtf(sum(x^2)/128) with the fp32
+ *               sum taken by one pairwise tree over the 128 channels (at stride 64,
+ *               32, ..., 1, element c < stride adds element c + stride)
  *   then        s = (hi - lo)/L (L = 2^bits - 1), scale = fp16(s), zero = fp16(lo)
  *               (both saturated to +-65504, round to nearest even),
  *               r = scale == 0 ? 0 : 1/scale, code = clamp(rint((x - zero)*r), 0, L).

@@ -16,7 +16,7 @@ import torch
 
 import oracle
 from decode_attention_kvq_amd import api, calib, synth
-from helpers import describe_mismatch, f16_ulp_distance, pool_codes
+from helpers import describe_mismatch, f16_ulp_distance, pool_codes, rms_order_rows
 
 pytestmark = pytest.mark.gpu
 
@@ -34,7 +34,8 @@ def _tie_row(levels):
 
 def _special_rows(x, rng):
     """Overwrite some token rows with edge cases: constant, zeros, +-0, integers, heavy
-    tails, tiny and huge magnitudes, and exact rounding ties at 2, 3 and 4 bits."""
+    tails, tiny and huge magnitudes, exact rounding ties at 2, 3 and 4 bits, and groups
+    whose RMS bound depends on the order of the sum of squares."""
     n = x.shape[0]
     if n > 8:
         x[1] = 0.37
@@ -48,6 +49,10 @@ def _special_rows(x, rng):
         x[8] = _tie_row(3)
         x[9] = _tie_row(7)
         x[10] = _tie_row(15)
+    if n > 13:
+        rows, _ = rms_order_rows()       # sums of squares that depend on the tree's order
+        x[11] = rows[0]
+        x[12] = rows[1]
     return x
 
 
