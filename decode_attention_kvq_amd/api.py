@@ -37,6 +37,17 @@ def _stream(stream):
     return C.c_void_p(s.cuda_stream)
 
 
+def _shape(t, name, *dims):
+    """Raises ValueError unless t (when given) has exactly the shape dims (None: any size).
+    Runs before anything reaches the library: a short tensor would be read past its end on
+    the device."""
+    if t is None:
+        return
+    if t.dim() != len(dims) or any(d is not None and s != d for s, d in zip(t.shape, dims)):
+        want = "[" + ", ".join("*" if d is None else str(d) for d in dims) + "]"
+        raise ValueError(f"{name} has shape {list(t.shape)}, expected {want}")
+
+
 def _dev(t, name, dtype=None):
     if t is None:
         return
@@ -63,7 +74,8 @@ class KVCache:
         shape_v = (num_pages, num_kv_heads, block_bytes(bits_v))
         self.k_pages = torch.zeros(shape_k, dtype=torch.uint8, device=device) if k_pages is None else k_pages
         self.v_pages = torch.zeros(shape_v, dtype=torch.uint8, device=device) if v_pages is None else v_pages
-        assert tuple(self.k_pages.shape) == shape_k and tuple(self.v_pages.shape) == shape_v
+        _shape(self.k_pages, "k_pages", *shape_k)
+        _shape(self.v_pages, "v_pages", *shape_v)
         _dev(self.k_pages, "k_pages", torch.uint8)
         _dev(self.v_pages, "v_pages", torch.uint8)
 
@@ -77,11 +89,13 @@ class KVCache:
 def kvq_quantize_append(cache: KVCache, k: torch.Tensor, v: torch.Tensor, slot_mapping: torch.Tensor,
                         t_k: torch.Tensor | None = None, stream=None) -> None:
     """k, v: [n, kv_heads, 128] (f32/bf16/f16); slot_mapping: [n] int64; t_k: [kv_heads,128,128]."""
+    H = cache.num_kv_heads
+    _shape(k, "k", None, H, HEAD_DIM)
+    n = k.shape[0]
+    _shape(v, "v", n, H, HEAD_DIM); _shape(slot_mapping, "slot_mapping", n)
+    _shape(t_k, "t_k", H, HEAD_DIM, HEAD_DIM)
     _dev(k, "k"); _dev(v, "v", k.dtype); _dev(slot_mapping, "slot_mapping", torch.int64)
     _dev(t_k, "t_k", k.dtype)
-    n = k.shape[0]
-    assert k.shape == (n, cache.num_kv_heads, HEAD_DIM) and v.shape == k.shape
-    assert slot_mapping.shape == (n,)
     d = cache.desc()
     check(load().kvq_quantize_append(C.byref(d), _ptr(k), _ptr(v), _DTYPES[k.dtype], n,
                                      _ptr(slot_mapping), _ptr(t_k), _DTYPES[k.dtype], _stream(stream)))
@@ -92,15 +106,28 @@ def decode_workspace_bytes(cache: KVCache, batch: int, num_q_heads: int, max_seq
     return int(load().kvq_decode_workspace_bytes(C.byref(d), batch, num_q_heads, max_seq_len))
 
 
+def _read_shapes(cache, q, block_table, seq_lens, t_k_inv_t, out, win_rows=None):
+    """Shape checks shared by the read calls; returns (B, Hq)."""
+    H = cache.num_kv_heads
+    _shape(q, "q", None, None, HEAD_DIM)
+    B, Hq = q.shape[0], q.shape[1]
+    if Hq % H != 0:
+        raise ValueError(f"q has {Hq} heads, not a multiple of the cache's {H} KV heads")
+    _shape(block_table, "block_table", B, None); _shape(seq_lens, "seq_lens", B)
+    _shape(win_rows, "win_rows", B)
+    _shape(t_k_inv_t, "t_k_inv_t", H, HEAD_DIM, HEAD_DIM); _shape(out, "out", B, Hq, HEAD_DIM)
+    return B, Hq
+
+
 def kvq_decode_attn(cache: KVCache, q: torch.Tensor, block_table: torch.Tensor, seq_lens: torch.Tensor,
                     max_seq_len: int, t_k_inv_t: torch.Tensor | None = None, sm_scale: float | None = None,
                     out: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
                     stream=None) -> torch.Tensor:
     """q: [B, Hq, 128]; block_table: [B, max_pages] int32; seq_lens: [B] int32.
     Returns out [B, Hq, 128] fp32 in the transformed value basis."""
+    B, Hq = _read_shapes(cache, q, block_table, seq_lens, t_k_inv_t, out)
     _dev(q, "q"); _dev(block_table, "block_table", torch.int32); _dev(seq_lens, "seq_lens", torch.int32)
     _dev(t_k_inv_t, "t_k_inv_t", torch.float32)
-    B, Hq, _ = q.shape
     if out is None:
         out = torch.empty((B, Hq, HEAD_DIM), dtype=torch.float32, device=q.device)
     _dev(out, "out", torch.float32)
@@ -125,13 +152,14 @@ def kvq_decode_step(cache: KVCache, q: torch.Tensor, k_new: torch.Tensor, v_new:
                     stream=None) -> torch.Tensor:
     """Append each sequence's new token (k_new, v_new: [B, kv_heads, 128]; new_slots: [B]
     int64, the slot of position seq_lens[b]-1) and decode, in one launch.  Returns out."""
+    B, Hq = _read_shapes(cache, q, block_table, seq_lens, t_k_inv_t, out)
+    H = cache.num_kv_heads
+    _shape(k_new, "k_new", B, H, HEAD_DIM); _shape(v_new, "v_new", B, H, HEAD_DIM)
+    _shape(new_slots, "new_slots", B); _shape(t_k, "t_k", H, HEAD_DIM, HEAD_DIM)
     _dev(q, "q"); _dev(k_new, "k_new", q.dtype); _dev(v_new, "v_new", q.dtype)
     _dev(new_slots, "new_slots", torch.int64); _dev(t_k, "t_k", q.dtype)
     _dev(block_table, "block_table", torch.int32); _dev(seq_lens, "seq_lens", torch.int32)
     _dev(t_k_inv_t, "t_k_inv_t", torch.float32)
-    B, Hq, _ = q.shape
-    assert k_new.shape == (B, cache.num_kv_heads, HEAD_DIM) and v_new.shape == k_new.shape
-    assert new_slots.shape == (B,)
     if out is None:
         out = torch.empty((B, Hq, HEAD_DIM), dtype=torch.float32, device=q.device)
     _dev(out, "out", torch.float32)
@@ -152,8 +180,10 @@ def kvq_decode_step(cache: KVCache, q: torch.Tensor, k_new: torch.Tensor, v_new:
 def kvq_dequant(cache: KVCache, which: int, slots: torch.Tensor, out: torch.Tensor | None = None,
                 stream=None) -> torch.Tensor:
     """which = 0 keys, 1 values; slots: [n] int64 -> [n, kv_heads, 128] fp32."""
-    _dev(slots, "slots", torch.int64)
+    _shape(slots, "slots", None)
     n = slots.shape[0]
+    _shape(out, "out", n, cache.num_kv_heads, HEAD_DIM)
+    _dev(slots, "slots", torch.int64)
     if out is None:
         out = torch.zeros((n, cache.num_kv_heads, HEAD_DIM), dtype=torch.float32, device=slots.device)
     _dev(out, "out", torch.float32)
@@ -176,7 +206,8 @@ class Window:
         shape = (num_rows, sink + keep + flush, cache.num_kv_heads, HEAD_DIM)
         self.k_win = torch.zeros(shape, dtype=dtype, device=device) if k_win is None else k_win
         self.v_win = torch.zeros(shape, dtype=dtype, device=device) if v_win is None else v_win
-        assert tuple(self.k_win.shape) == shape and tuple(self.v_win.shape) == shape
+        _shape(self.k_win, "k_win", *shape)
+        _shape(self.v_win, "v_win", *shape)
         _dev(self.k_win, "k_win", dtype)
         _dev(self.v_win, "v_win", dtype)
 
@@ -190,11 +221,18 @@ def kvq_window_prefill(cache: KVCache, win: Window, k: torch.Tensor, v: torch.Te
                        win_rows: torch.Tensor | None = None, t_k: torch.Tensor | None = None,
                        stream=None) -> None:
     """Fresh prompts packed as k, v [n, kv_heads, 128] with offsets cu_seqlens [B+1] int32."""
+    H = cache.num_kv_heads
+    _shape(k, "k", None, H, HEAD_DIM)
+    _shape(v, "v", k.shape[0], H, HEAD_DIM)
+    _shape(cu_seqlens, "cu_seqlens", None)
+    if cu_seqlens.shape[0] < 1:
+        raise ValueError("cu_seqlens has shape [0], expected [batch + 1]")
+    _shape(block_table, "block_table", cu_seqlens.shape[0] - 1, None)
+    _shape(win_rows, "win_rows", cu_seqlens.shape[0] - 1); _shape(t_k, "t_k", H, HEAD_DIM, HEAD_DIM)
     _dev(k, "k", win.dtype); _dev(v, "v", win.dtype); _dev(cu_seqlens, "cu_seqlens", torch.int32)
     _dev(block_table, "block_table", torch.int32); _dev(win_rows, "win_rows", torch.int32)
     _dev(t_k, "t_k", win.dtype)
     n = k.shape[0]
-    assert k.shape == (n, cache.num_kv_heads, HEAD_DIM) and v.shape == k.shape
     B = cu_seqlens.shape[0] - 1
     d, w = cache.desc(), win.desc()
     check(load().kvq_window_prefill(C.byref(d), C.byref(w), _ptr(k), _ptr(v), B, _ptr(cu_seqlens), n,
@@ -225,10 +263,10 @@ def kvq_window_decode_attn(cache: KVCache, win: Window, q: torch.Tensor, block_t
                            out: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
                            stream=None) -> torch.Tensor:
     """Attention over a windowed cache (state after every waiting batch was quantized)."""
+    B, Hq = _read_shapes(cache, q, block_table, seq_lens, t_k_inv_t, out, win_rows)
     _dev(q, "q", win.dtype); _dev(block_table, "block_table", torch.int32)
     _dev(seq_lens, "seq_lens", torch.int32); _dev(win_rows, "win_rows", torch.int32)
     _dev(t_k_inv_t, "t_k_inv_t", torch.float32)
-    B, Hq, _ = q.shape
     out, workspace, ws_bytes = _window_out_ws(cache, win, q, max_seq_len, out, workspace)
     if sm_scale is None:
         sm_scale = 1.0 / math.sqrt(HEAD_DIM)
@@ -248,12 +286,14 @@ def kvq_window_decode_step(cache: KVCache, win: Window, q: torch.Tensor, k_new: 
                            workspace: torch.Tensor | None = None, stream=None) -> torch.Tensor:
     """One decode step: seq_lens [B] counts the new position, whose key and value are
     k_new, v_new [B, kv_heads, 128]; attention, then the flush of the batch it made eligible."""
+    B, Hq = _read_shapes(cache, q, block_table, seq_lens, t_k_inv_t, out, win_rows)
+    H = cache.num_kv_heads
+    _shape(k_new, "k_new", B, H, HEAD_DIM); _shape(v_new, "v_new", B, H, HEAD_DIM)
+    _shape(t_k, "t_k", H, HEAD_DIM, HEAD_DIM)
     _dev(q, "q", win.dtype); _dev(k_new, "k_new", win.dtype); _dev(v_new, "v_new", win.dtype)
     _dev(block_table, "block_table", torch.int32); _dev(seq_lens, "seq_lens", torch.int32)
     _dev(win_rows, "win_rows", torch.int32); _dev(t_k, "t_k", win.dtype)
     _dev(t_k_inv_t, "t_k_inv_t", torch.float32)
-    B, Hq, _ = q.shape
-    assert k_new.shape == (B, cache.num_kv_heads, HEAD_DIM) and v_new.shape == k_new.shape
     out, workspace, ws_bytes = _window_out_ws(cache, win, q, max_seq_len, out, workspace)
     if sm_scale is None:
         sm_scale = 1.0 / math.sqrt(HEAD_DIM)
