@@ -15,18 +15,22 @@
 //    (nontemporal) of page i + PIPE are issued when page i has been used, so PIPE pages
 //    are in flight per wave.
 // Contractions, fp32 accumulation:
-//   scores  S[token][col] = codes_K[token][ch] . q''[ch][col]
+//   scores  S[token][col] = codes_K[token][ch] . q'[ch][col]
 //   output  O[ch][col]   += codes_V[ch][token] . P~[token][col]
-// 2-bit keys use the scaled fp4 x fp6 16x16x128 product: a 2-bit code in the low bits of
-// an fp4 nibble is the exact value code/2, so one AND yields 8 operands, and q' is carried
-// as three fp6 terms with per-term E8M0 scales (about 12 significant bits, like fp16).
-// 4-bit keys and the P.V product use 16x16x32 fp16 products: an AND of the packed word
-// with a mask leaves, in each 16-bit half, one code at bit b*e of the mantissa of a
-// subnormal fp16, i.e. the exact value code * 2^(b*e) * 2^-24 (codes in the top bits of a
-// half are shifted down first); the factor 2^-(b*e) is folded into the other operand.
+// Keys of every width use the scaled fp4 x fp6 16x16x128 product: a 2-bit code (or a
+// 2-bit slice of a 3- or 4-bit code) in the low bits of an fp4 nibble is the exact value
+// code/2, so one AND yields 8 operands; a 4-bit code's high pair weighs 4 through the A
+// operand's scale.  q' is carried as fp6 terms with per-term E8M0 scales: three (about 12
+// significant bits), and a fourth on pages whose scores are large.
+// The P.V product uses 16x16x32 fp16 products: an AND of the packed value word with a
+// mask leaves, in each 16-bit half, one code at bit b*e of the mantissa of a subnormal
+// fp16, i.e. the exact value code * 2^(b*e) * 2^-24 (codes in the top bits of a half are
+// shifted down first); the factor 2^-(b*e) is folded into P~.
 // Scale and zero are applied outside the products:
 //   score_t = s_t * (q . code_t) + z_t * sum(q)
 //   out     = (sum_t p_t s_t code_t + sum_t p_t z_t) / sum_t p_t
+// P~ = p s_v 2^(S - b*e) is fp16; the exponent S follows the largest P~ of each page, so the
+// tokens that carry the weight keep fp16's full precision whatever their value scales.
 //
 // Column packing.  The 16 columns hold GP >= G query heads repeated in 16/GP blocks;
 // score tile b (16 tokens) only feeds the columns of block b % (16/GP), so one 16x16
@@ -105,18 +109,6 @@ __device__ __forceinline__ float col_sum(float v) {
   return __builtin_bit_cast(float, (uint32_t)c[0]) + __builtin_bit_cast(float, (uint32_t)c[1]);
 }
 
-// Channel of the K-code operand element j at K-step s for lane group kg.
-template <int BK> __host__ __device__ constexpr int k_channel(int s, int kg, int j) {
-  if constexpr (BK == 2) {
-    return 16 * (2 * kg + s / 2) + (4 * (s % 2) + j / 2) + 8 * (j % 2);
-  } else {
-    return 8 * (4 * kg + s) + j / 2 + 4 * (j % 2);
-  }
-}
-// Position class of channel c in a K row word.
-template <int BK> __host__ __device__ constexpr int k_channel_class(int c) {
-  return BK == 2 ? pair_class<2>((c % 16) % 8) : pair_class<4>((c % 8) % 4);
-}
 // Token (0..15 within the lane group) of V operand element j at step s, and its class.
 template <int BV> __host__ __device__ constexpr int v_token(int s, int j) {
   return BV == 2 ? (4 * s + j / 2) + 8 * (j % 2) : 8 * s + j / 2 + 4 * (j % 2);
@@ -125,29 +117,42 @@ template <int BV> __host__ __device__ constexpr int v_token_class(int u) {
   return BV == 2 ? pair_class<2>(u % 8) : pair_class<4>((u % 8) % 4);
 }
 
-// ---- 2-bit keys on the scaled fp4 x fp6 matrix-core product (16x16x128) ----
+// ---- keys on the scaled fp4 x fp6 matrix-core product (16x16x128) ----
 // A 2-bit code c in the low two bits of an fp4 (e2m1) nibble is the exact value c/2, so an
-// AND with 0x33333333 turns a packed word into 8 fp4 operands (its even codes) and a shift
-// plus AND gives the odd ones.  Lane group kg reads words 2kg, 2kg+1 of the token's row
-// (channels 32kg .. 32kg+31); operand element j of the lane is channel k2_channel(kg, j).
-// fp4 and fp6 operands of this product share one layout (lane group g, element j is
-// contraction index 32g + j), and each lane's 32 elements carry their own E8M0 scale.
-__host__ __device__ constexpr int k2_channel(int kg, int j) {
-  return 32 * kg + 16 * (j / 16) + 2 * (j % 8) + (j / 8) % 2;
+// AND with 0x33333333 turns a packed 2-bit word into 8 fp4 operands (its even codes) and a
+// shift plus AND gives the odd ones.  A 4-bit code is two such pairs: the same AND leaves
+// bits 0-1 of each code in place and a shift by 2 first gives bits 2-3, whose product
+// weighs 4 through the A operand's E8M0 scale.  3-bit codes add their bit-2 plane as the
+// fp4 value 2.  Lane group kg reads the channels 32kg .. 32kg+31 of its token's row;
+// operand element j of the lane is channel key_channel<BK>(kg, j).  fp4 and fp6 operands of
+// this product share one layout (lane group g, element j is contraction index 32g + j),
+// and each lane's 32 elements carry their own E8M0 scale.
+template <int BK> __host__ __device__ constexpr int key_channel(int kg, int j) {
+  return BK == 4 ? 32 * kg + j : 32 * kg + 16 * (j / 16) + 2 * (j % 8) + (j / 8) % 2;
 }
 constexpr uint32_t kFp4CodeMask = 0x33333333u;
 constexpr uint32_t kFp4HighMask = 0x44444444u;   // bit 2 of every nibble: the fp4 value 2
-constexpr int kQTerms = 3;          // fp6 terms of q'': about 12 significant bits together
+constexpr int kUnitScale = 0x7F7F7F7F;           // E8M0 2^0 in every byte
+constexpr int kTimes4Scale = 0x81818181;         // E8M0 2^2 in every byte
+// q' is carried as fp6 terms (4 significant bits each, scales 4 binades apart).  Three
+// represent it to about 2^-12 of its largest element; a fourth, to about 2^-16, joins the
+// products of a page whose largest score (log2 units) exceeds kBigScore in magnitude, where
+// a relative score error of 2^-12 would move the softmax weights by more than the
+// output's bound allows.
+constexpr int kQTerms = 4;
+constexpr int kQBase = 3;
+constexpr float kBigScore = 24.0f;
 
 typedef int v8i __attribute__((ext_vector_type(8)));
-// D = A(fp4, unit scales) . B(fp6 e2m3, scale byte `opsel` of sb) + C; opsel is a constant
+// D = A(fp4, scale sa) . B(fp6 e2m3, scale byte `opsel` of sb) + C; opsel is a constant
 // after unrolling.
-__device__ __forceinline__ f32x4 mma_fp4_fp6(int opsel, const v8i& a, const v8i& b, f32x4 c, int sb) {
+__device__ __forceinline__ f32x4 mma_fp4_fp6(int opsel, const v8i& a, const v8i& b, f32x4 c, int sb,
+                                             int sa = kUnitScale) {
   switch (opsel) {
-    case 0: return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 4, 2, 0, 0x7F7F7F7F, 0, sb);
-    case 1: return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 4, 2, 0, 0x7F7F7F7F, 1, sb);
-    case 2: return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 4, 2, 0, 0x7F7F7F7F, 2, sb);
-    default: return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 4, 2, 0, 0x7F7F7F7F, 3, sb);
+    case 0: return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 4, 2, 0, sa, 0, sb);
+    case 1: return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 4, 2, 0, sa, 1, sb);
+    case 2: return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 4, 2, 0, sa, 2, sb);
+    default: return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 4, 2, 0, sa, 3, sb);
   }
 }
 
@@ -272,9 +277,8 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
 
   // merge buffers (per wave: 16 columns x 128 channels, then 16 x (m, l))
   __shared__ __attribute__((aligned(16))) uint8_t smem[kWaves * 16 * (kHeadDim + 2) * 4];
-  // prologue scratch: q, then q'; the fp16 operand; two constants per head
+  // prologue scratch: q, then q'; per head the sum of q' as carried by kQBase and kQTerms terms
   __shared__ __attribute__((aligned(16))) float qs[GP * kHeadDim];
-  __shared__ __attribute__((aligned(16))) uint16_t qh[GP * kHeadDim];
   __shared__ float hconst[GP * 2];
 
   // ---- this wave's pages ----
@@ -384,18 +388,29 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
       }
   }
   lds_barrier();
-  // 2-bit keys: q' as three fp6 terms t_k with scales 2^(e1 - 4k), e1 per head so that
-  // max|q'| 2^-e1 <= 7.5; each term holds the previous remainder to within a quarter of its
-  // scale, so the sum of the three represents q' to about 2^-12 of its largest element.
-  // The product with the fp4 codes (value c/2) gives half of q'.code: F = 2.
+  // q' as fp6 terms t_k with scales 2^(e1 - 4k), e1 per head so that max|q'| 2^-e1 <= 7.5;
+  // each term holds the previous remainder to within a quarter of its scale.  The product
+  // with the fp4 codes (value c/2) gives half of q'.code: F = 2.
   v8i bq6[kQTerms];
   int sreg[kQTerms];
-  u32x4 bq[BK != 4 ? 1 : NB][4];     // fp16 operands (4-bit keys)
   const int gq = n % GP;
-  if constexpr (BK != 4) {
-    uint8_t* qcode = smem;                                         // [term][head][channel]
-    uint32_t* qpack = reinterpret_cast<uint32_t*>(smem + kQTerms * GP * kHeadDim);  // [term][kg][head][6]
-    int* qexp = reinterpret_cast<int*>(qpack + kQTerms * 4 * GP * 6);
+  uint8_t* qcode = smem;                                           // [term][head][channel]
+  uint32_t* qpack = reinterpret_cast<uint32_t*>(smem + kQTerms * GP * kHeadDim);  // [term][kg][head][6]
+  int* qexp = reinterpret_cast<int*>(qpack + kQTerms * 4 * GP * 6);
+  // fp6 operand and scale register of term k for this lane
+  auto term_operand = [&](int k, v8i& bq, int& sr) {
+#pragma unroll
+    for (int d = 0; d < 6; ++d) bq[d] = (int)qpack[((k * 4 + kg) * GP + gq) * 6 + d];
+    bq[6] = 0;
+    bq[7] = 0;
+    // scale byte t (selected per tile by op_sel): the term's scale for this lane's column
+    // block, 2^-127 (contributes nothing) for the others
+    uint32_t sc = 0;
+#pragma unroll
+    for (int t = 0; t < NB; ++t) sc |= (beta == t ? (uint32_t)(127 + qexp[gq] - 4 * k) : 0u) << (8 * t);
+    sr = (int)sc;
+  };
+  {
     for (int g = wave; g < GP; g += kWaves) {
       const float a0 = g < G ? qs[g * kHeadDim + lane] : 0.0f, a1 = g < G ? qs[g * kHeadDim + lane + 64] : 0.0f;
       float amax = fmaxf(fabsf(a0), fabsf(a1));
@@ -406,8 +421,8 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
         const int E = ilogbf(amax);
         e1 = ldexpf(amax, 2 - E) <= 7.5f ? E - 2 : E - 1;
       }
-      e1 = max(e1, -118);                  // the last term's scale stays a normal E8M0 value
-      float r0 = a0, r1 = a1, qsum = 0.0f;
+      e1 = max(e1, -126 + 4 * (kQTerms - 1));   // the last term's scale stays a normal E8M0 value
+      float r0 = a0, r1 = a1, qsum3 = 0.0f, qsum4 = 0.0f;
 #pragma unroll
       for (int k = 0; k < kQTerms; ++k) {
         const int e = e1 - 4 * k;
@@ -415,15 +430,19 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
         const float v0 = ldexpf(e2m3_decode(c0), e), v1 = ldexpf(e2m3_decode(c1), e);
         r0 -= v0;
         r1 -= v1;
-        qsum += v0 + v1;
+        if (k < kQBase) qsum3 += v0 + v1;
+        qsum4 += v0 + v1;
         qcode[(k * GP + g) * kHeadDim + lane] = (uint8_t)c0;
         qcode[(k * GP + g) * kHeadDim + lane + 64] = (uint8_t)c1;
       }
 #pragma unroll
-      for (int d = 1; d < 64; d <<= 1) qsum += __shfl_xor(qsum, d);
+      for (int d = 1; d < 64; d <<= 1) {
+        qsum3 += __shfl_xor(qsum3, d);
+        qsum4 += __shfl_xor(qsum4, d);
+      }
       if (lane == 0) {
-        hconst[2 * g] = qsum;
-        hconst[2 * g + 1] = 2.0f;
+        hconst[2 * g] = qsum3;
+        hconst[2 * g + 1] = qsum4;
         qexp[g] = e1;
       }
     }
@@ -435,7 +454,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
       uint32_t word = 0;
       const int j0 = (32 * d) / 6, j1 = min(31, (32 * d + 31) / 6);
       for (int j = j0; j <= j1; ++j) {
-        const uint32_t c = src[k2_channel(kgi, j)];
+        const uint32_t c = src[key_channel<BK>(kgi, j)];
         const int sh = 6 * j - 32 * d;
         word |= sh >= 0 ? c << sh : c >> (-sh);
       }
@@ -443,60 +462,10 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
     }
     lds_barrier();
 #pragma unroll
-    for (int k = 0; k < kQTerms; ++k) {
-#pragma unroll
-      for (int d = 0; d < 6; ++d) bq6[k][d] = (int)qpack[((k * 4 + kg) * GP + gq) * 6 + d];
-      bq6[k][6] = 0;
-      bq6[k][7] = 0;
-      // scale byte t (selected per tile by op_sel): the term's scale for this lane's column
-      // block, 2^-127 (contributes nothing) for the others
-      uint32_t s = 0;
-#pragma unroll
-      for (int t = 0; t < NB; ++t) s |= (beta == t ? (uint32_t)(127 + qexp[gq] - 4 * k) : 0u) << (8 * t);
-      sreg[k] = (int)s;
-    }
-  } else {
-  // fp16 operand q''[c] = q'[c] * 2^(E - BK*e(c)), E per head so that max|q''| < 2^15
-  for (int g = wave; g < G; g += kWaves) {
-    const float a0 = qs[g * kHeadDim + lane], a1 = qs[g * kHeadDim + lane + 64];
-    float amax = fmaxf(fabsf(a0), fabsf(a1));
-#pragma unroll
-    for (int d = 1; d < 64; d <<= 1) amax = fmaxf(amax, __shfl_xor(amax, d));
-    const int E = amax > 0.0f ? 14 - ilogbf(amax) : 0;
-    float qsum = 0.0f;
-#pragma unroll
-    for (int k = 0; k < 2; ++k) {
-      const int c = lane + 64 * k;
-      const int sh = BK * k_channel_class<BK>(c);
-      const uint16_t hbits = f32_to_f16_bits(ldexpf(k ? a1 : a0, E - sh));
-      qh[g * kHeadDim + c] = hbits;
-      qsum += ldexpf(f16_bits_to_f32(hbits), sh - E);
-    }
-#pragma unroll
-    for (int d = 1; d < 64; d <<= 1) qsum += __shfl_xor(qsum, d);
-    if (lane == 0) {
-      hconst[2 * g] = qsum;
-      hconst[2 * g + 1] = ldexpf(1.0f, 24 - E);
-    }
+    for (int k = 0; k < kQTerms; ++k) term_operand(k, bq6[k], sreg[k]);
   }
-  lds_barrier();
-  // B operand of K-step s for this lane (column n = head n % GP, lane group kg), masked per
-  // column block: block beta's operand is the lane's own, the others are zero
-#pragma unroll
-  for (int s = 0; s < 4; ++s) {
-    u32x4 w;
-#pragma unroll
-    for (int jj = 0; jj < 4; ++jj) {
-      const uint32_t lo = gq < G ? qh[gq * kHeadDim + k_channel<BK>(s, kg, 2 * jj)] : 0u;
-      const uint32_t hi = gq < G ? qh[gq * kHeadDim + k_channel<BK>(s, kg, 2 * jj + 1)] : 0u;
-      w[jj] = lo | (hi << 16);
-    }
-#pragma unroll
-    for (int bb = 0; bb < NB; ++bb) bq[bb][s] = (beta == bb) ? w : u32x4{0u, 0u, 0u, 0u};
-  }
-  }
-  const float F = gq < G ? hconst[2 * gq + 1] : 1.0f;                  // score = F * x'
-  const float qsf = gq < G ? hconst[2 * gq] / hconst[2 * gq + 1] : 0.0f;
+  constexpr float F = 2.0f;                                              // score = F * x'
+  const float qsf3 = gq < G ? hconst[2 * gq] / F : 0.0f;
 
 
   // per (accumulator a, row r): token u = 4*(a*NB + beta) + r of this lane group
@@ -536,7 +505,8 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
     bmask[s] = ((t_lo % NB == beta) ? 0x0000FFFFu : 0u) | ((t_hi % NB == beta) ? 0xFFFF0000u : 0u);
   }
   float m = -__builtin_inff();   // running max of x' for this lane's column
-  int S = 30;
+  int S = 30;                    // P~ carries 2^(S - vcls)
+  int hmax = -128;               // exponent of the largest P~ accumulated so far (units of S)
 
   // ---- page walk: compute page i from ring slot i % PIPE, then refill the slot ----
   auto compute = [&](const PageRegs<BK, BV, A>& pr, int i) {
@@ -544,19 +514,32 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
     const bool partial = valid_tokens < kPageTokens;
 
     // ---- scores: tile t4 = tokens 16*(n/4) + 4*t4 + n%4 in rows n ----
+    // one 16x16x128 product per tile, key plane and q' term; the op_sel'd scale byte keeps
+    // tile t4 out of every column block but t4 % NB
     f32x4 sacc[A];
 #pragma unroll
     for (int a = 0; a < A; ++a) sacc[a] = f32x4{};
-    if constexpr (BK != 4) {
-      // one 16x16x128 product per tile and fp6 term; the op_sel'd scale byte keeps tile t4
-      // out of every column block but t4 % NB
+    // products of tile t4 with the q' terms K0 .. K0 + NT - 1
+    using std::integral_constant;
+    auto key_products = [&](int t4, auto k_first, auto k_count) {
+      constexpr int K0 = decltype(k_first)::value, NT = decltype(k_count)::value;
+      if constexpr (BK == 4) {
+        const u32x4 w = pr.k[t4];
+        const v8i lo = {(int)(w[0] & kFp4CodeMask), (int)(w[1] & kFp4CodeMask), (int)(w[2] & kFp4CodeMask),
+                        (int)(w[3] & kFp4CodeMask), 0, 0, 0, 0};
+        const v8i hi = {(int)((w[0] >> 2) & kFp4CodeMask), (int)((w[1] >> 2) & kFp4CodeMask),
+                        (int)((w[2] >> 2) & kFp4CodeMask), (int)((w[3] >> 2) & kFp4CodeMask), 0, 0, 0, 0};
 #pragma unroll
-      for (int t4 = 0; t4 < 4; ++t4) {
+        for (int k = K0; k < K0 + NT; ++k) {
+          sacc[t4 / NB] = mma_fp4_fp6(t4 % NB, lo, bq6[k], sacc[t4 / NB], sreg[k]);
+          sacc[t4 / NB] = mma_fp4_fp6(t4 % NB, hi, bq6[k], sacc[t4 / NB], sreg[k], kTimes4Scale);
+        }
+      } else {
         const uint32_t w0 = pr.k[t4][0], w1 = pr.k[t4][1];
         const v8i av = {(int)(w0 & kFp4CodeMask), (int)((w0 >> 2) & kFp4CodeMask), (int)(w1 & kFp4CodeMask),
                         (int)((w1 >> 2) & kFp4CodeMask), 0, 0, 0, 0};
 #pragma unroll
-        for (int k = 0; k < kQTerms; ++k) sacc[t4 / NB] = mma_fp4_fp6(t4 % NB, av, bq6[k], sacc[t4 / NB], sreg[k]);
+        for (int k = K0; k < K0 + NT; ++k) sacc[t4 / NB] = mma_fp4_fp6(t4 % NB, av, bq6[k], sacc[t4 / NB], sreg[k]);
         if constexpr (BK == 3) {
           // high plane: operand element (dword d, nibble i) is channel offset
           // 16(d/2) + d%2 + 2i, whose bit sits at 4i + d; shifted to bit 2 of the nibble it
@@ -565,41 +548,53 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
           const v8i ah = {(int)((h << 2) & kFp4HighMask), (int)((h << 1) & kFp4HighMask), (int)(h & kFp4HighMask),
                           (int)((h >> 1) & kFp4HighMask), 0, 0, 0, 0};
 #pragma unroll
-          for (int k = 0; k < kQTerms; ++k) sacc[t4 / NB] = mma_fp4_fp6(t4 % NB, ah, bq6[k], sacc[t4 / NB], sreg[k]);
+          for (int k = K0; k < K0 + NT; ++k) sacc[t4 / NB] = mma_fp4_fp6(t4 % NB, ah, bq6[k], sacc[t4 / NB], sreg[k]);
         }
       }
-    } else
+    };
 #pragma unroll
-    for (int t4 = 0; t4 < 4; ++t4) {
-      uint32_t kw[BK == 2 ? 2 : 4];
-#pragma unroll
-      for (int e = 0; e < (BK == 2 ? 2 : 4); ++e) kw[e] = pr.k[t4][e];
-#pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        const uint32_t w = BK == 2 ? kw[s / 2] : kw[s];
-        const uint32_t ws = shifted<BK>(w);
-        u32x4 av;
-#pragma unroll
-        for (int jj = 0; jj < 4; ++jj) av[jj] = code_pair<BK>(w, ws, BK == 2 ? 4 * (s % 2) + jj : jj);
-        sacc[t4 / NB] = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(av), as_half8(bq[t4 % NB][s]),
-                                                              sacc[t4 / NB], 0, 0, 0);
-      }
-    }
+    for (int t4 = 0; t4 < 4; ++t4) key_products(t4, integral_constant<int, 0>{}, integral_constant<int, kQBase>{});
     // metadata of the lane's tokens (4 consecutive per tile: 8 bytes each).  The fp16
     // scales and zeros enter the arithmetic as fp16 operands of mixed fma (no conversions).
+    // score = s_k * (q' . code) + z_k * sum(q'), with sum(q') as the terms carry it
     float x[A][4];
+    auto token_scores = [&](float qsf) {
+#pragma unroll
+      for (int a = 0; a < A; ++a) {
+        // (the 8-byte pair is reinterpreted whole: building half pairs from its two words
+        // separately is miscompiled by this toolchain, which then reads only the first word)
+        const half4_t sk = __builtin_bit_cast(half4_t, pr.meta[a][0]);
+        const half4_t zk = __builtin_bit_cast(half4_t, pr.meta[a][1]);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float zq = __builtin_fmaf((float)zk[r], qsf, 0.0f);
+          x[a][r] = __builtin_fmaf(sacc[a][r], (float)sk[r], zq);
+        }
+      }
+      if (partial) {                        // absent tokens: no weight
+#pragma unroll
+        for (int a = 0; a < A; ++a)
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            x[a][r] = 16 * kg + 4 * (a * NB + beta) + r < valid_tokens ? x[a][r] : -__builtin_inff();
+      }
+      float mx = x[0][0];
+#pragma unroll
+      for (int a = 0; a < A; ++a)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) mx = fmaxf(mx, x[a][r]);
+      return col_max(mx);
+    };
+    float mx = token_scores(qsf3);
+    // (a column without tokens in a partial page has mx = -inf and takes the branch too)
+    if (__any(fabsf(mx) > kBigScore / F)) {
+#pragma unroll
+      for (int t4 = 0; t4 < 4; ++t4) key_products(t4, integral_constant<int, kQBase>{}, integral_constant<int, 1>{});
+      mx = token_scores(gq < G ? hconst[2 * gq + 1] / F : 0.0f);
+    }
     u32x2 svp[A], zvp[A];
 #pragma unroll
     for (int a = 0; a < A; ++a) {
-      // (the 8-byte pair is reinterpreted whole: building half pairs from its two words
-      // separately is miscompiled by this toolchain, which then reads only the first word)
-      const half4_t sk = __builtin_bit_cast(half4_t, pr.meta[a][0]);
-      const half4_t zk = __builtin_bit_cast(half4_t, pr.meta[a][1]);
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const float zq = __builtin_fmaf((float)zk[r], qsf, 0.0f);
-        x[a][r] = __builtin_fmaf(sacc[a][r], (float)sk[r], zq);
-      }
       svp[a] = pr.meta[a][2];
       zvp[a] = pr.meta[a][3];
     }
@@ -609,43 +604,20 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const bool ok = 16 * kg + 4 * (a * NB + beta) + r < valid_tokens;
-          x[a][r] = ok ? x[a][r] : -__builtin_inff();
           const uint32_t keep = ok ? 0xFFFFFFFFu : ((r & 1) ? 0x0000FFFFu : 0xFFFF0000u);
           svp[a][r >> 1] &= keep;
           zvp[a][r >> 1] &= keep;
         }
     }
     // ---- online softmax, per column ----
-    float mx = x[0][0];
-    uint32_t svm = 0;                      // largest value-scale bit pattern (s_v >= 0)
-#pragma unroll
-    for (int a = 0; a < A; ++a) {
-#pragma unroll
-      for (int r = 0; r < 4; ++r) mx = fmaxf(mx, x[a][r]);
-#pragma unroll
-      for (int e = 0; e < 2; ++e) svm = max(svm, max(svp[a][e] & 0xFFFFu, svp[a][e] >> 16));
-    }
-    mx = col_max(mx);
-    // Lazy rescaling.  The reference max m of a column moves only when the page's scores
-    // exceed it by more than kLag (log2 units), so p = 2^(F(x - m)) <= 2^kLag; S moves
-    // only when a value scale would push P~ = p s_v 2^(S - vcls) to 2^15 (fp16 range),
-    // and then kSMargin further, so that later pages rarely need it again.  Rescaling is
-    // wave-uniform, so an eager rule would run it whenever any of the 16 columns grows.
+    // Lazy maximum: the reference max m of a column moves only when the page's scores
+    // exceed it by more than kLag (log2 units), so p = 2^(F(x - m)) <= 2^kLag.  Rescaling
+    // is wave-uniform, so an eager rule would run it whenever any of the 16 columns grows.
     constexpr float kLag = 8.0f;
-    constexpr int kSMargin = 4;
-    // exponent bound of the column's largest value scale: s_v < 2^(ev+1) (fp16 bits;
-    // a subnormal scale counts as 2^-15)
-    const int svbits = col_max_i((int)svm);
-    const int e16 = (svbits >> 10) & 0x1F;
-    const int ev = svbits == 0 ? -30 : (e16 == 0 ? -15 : e16 - 15);
-    // (3-bit values: the high plane's P~ carries up to 4x more, two bits of headroom)
-    const int S_tight = (BV == 3 ? 12 : 14) - (int)kLag - ev;
-    const bool need_s = S_tight < S;
-    const int S_new = need_s ? S_tight - kSMargin : S;
     const bool need_m = F * (mx - m) > kLag;       // false when the column has no token here
-    const float m_new = need_m ? mx : m;
-    if (__any(need_m || need_s)) {
-      const float alpha = exp2f(F * (m - m_new) + (float)(S_new - S));
+    if (__any(need_m)) {
+      const float m_new = need_m ? mx : m;
+      const float alpha = exp2f(F * (m - m_new));
 #pragma unroll
       for (int mt = 0; mt < 8; ++mt) acc_o[mt] *= alpha;
 #pragma unroll
@@ -654,12 +626,12 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
         for (int r = 0; r < 4; ++r) {
           lsum[a][r] *= alpha;
           zacc[a][r] *= alpha;
-          nb[a][r] = (float)(S_new - vcls[a][r]) - F * m_new;
+          nb[a][r] = (float)(S - vcls[a][r]) - F * m_new;
         }
       m = m_new;
-      S = S_new;
     }
     float pt[A][4];
+    uint32_t pbits = 0;                    // largest P~ of the lane (P~ >= 0: bit patterns order)
 #pragma unroll
     for (int a = 0; a < A; ++a)
 #pragma unroll
@@ -670,7 +642,41 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
         lsum[a][r] += pe;
         zacc[a][r] = __builtin_fmaf(pe, (float)zvh[r], zacc[a][r]);
         pt[a][r] = __builtin_fmaf(pe, (float)svh[r], 0.0f);
+        pbits = max(pbits, __float_as_uint(pt[a][r]));
       }
+    // The P.V operand P~ = p s_v 2^(S - vcls) is fp16.  S follows the tokens that carry the
+    // weight: it moves when the column's largest P~ of the page leaves [2^kPtLo, 2^(kPtHi+1)),
+    // to 2^kPtTarget, which leaves 2^kLag for later pages' p.  A token whose P~ is below the
+    // fp16 normal range then weighs less than 2^-(14 + kPtLo) of the page's largest, and its
+    // rounding error is below 2^-(25 + kPtLo) of it.  An upward move is capped so that the
+    // largest P~ already accumulated stays below 2^kStateMax in the new units (fp32 state).
+    // The page's own sums are already in lsum / zacc: powers of two scale them exactly.
+    // (3-bit values: the high plane's P~ carries up to 2^6 more.)
+    constexpr int kPtHi = BV == 3 ? 8 : 14;
+    constexpr int kPtTarget = kPtHi - (int)kLag - 2;
+    constexpr int kPtLo = kPtTarget - 8;
+    constexpr int kStateMax = 48;
+    const int pcol = col_max_i((int)pbits);
+    const int e = (pcol >> 23) - 127;                 // exponent of the largest P~ (pcol > 0)
+    const bool need_s = pcol != 0 && (e > kPtHi || e < kPtLo);
+    if (__any(need_s)) {
+      const int d = need_s ? min(kPtTarget - e, kStateMax - hmax) : 0;
+      const float f = __builtin_amdgcn_ldexpf(1.0f, d);
+#pragma unroll
+      for (int mt = 0; mt < 8; ++mt) acc_o[mt] *= f;
+#pragma unroll
+      for (int a = 0; a < A; ++a)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          lsum[a][r] *= f;
+          zacc[a][r] *= f;
+          pt[a][r] *= f;
+          nb[a][r] += (float)d;
+        }
+      S += d;
+      hmax += d;
+    }
+    hmax = max(hmax, pcol != 0 ? e : -128);
 
     // ---- P.V: B operand element (s, 2*jj + h) is token u = v_token(s, 2jj+h), i.e. tile
     // b(s, h) = u/4, row jj; the lane feeds only its own tiles, the rest of the operand is 0

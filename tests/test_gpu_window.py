@@ -10,7 +10,7 @@ import torch
 
 import oracle
 from decode_attention_kvq_amd import api, calib, synth
-from helpers import f16_ulp_distance, pool_codes, row_rel_err
+from helpers import f16_ulp_distance, pool_codes, row_rel_err, rare_event_bound
 
 pytestmark = pytest.mark.gpu
 
@@ -325,7 +325,8 @@ def test_full_size_window_step_sampled():
     page_slots = pg * 64 + np.arange(64)
     gc, gs, gz = pool_codes(cache.k_pages.cpu().numpy(), 0, w.bits_k, page_slots)
     oc, os_, oz = pool_codes(kp2, 0, w.bits_k, page_slots)
-    assert np.mean(gc != oc) <= 1e-3                          # fp32 vs fp64 transform sums
+    assert np.mean(gc != oc) <= 1e-4                          # fp32 vs fp64 transform sums
+    assert np.sum((gs != os_) | (gz != oz)) <= rare_event_bound(gs.size)
     assert np.all(f16_ulp_distance(gs, os_) <= 1) and np.all(f16_ulp_distance(gz, oz) <= 1)
     untouched = [x for x in range(B * pps) if x != pg]
     assert torch.equal(cache.v_pages[untouched].cpu(), torch.from_numpy(vp[untouched]))
