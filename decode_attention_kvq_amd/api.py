@@ -144,6 +144,25 @@ def kvq_decode_attn(cache: KVCache, q: torch.Tensor, block_table: torch.Tensor, 
     return out
 
 
+def kvq_decode_attn_noalloc(cache: KVCache, q: torch.Tensor, block_table: torch.Tensor,
+                            seq_lens: torch.Tensor, max_seq_len: int, out: torch.Tensor,
+                            t_k_inv_t: torch.Tensor | None = None, sm_scale: float | None = None,
+                            stream=None) -> torch.Tensor:
+    """kvq_decode_attn without a workspace, for callers that cannot allocate: `out`
+    [B, Hq, 128] fp32 is the caller's; the split partials use the library's device array
+    (KVQ_NOALLOC_SCRATCH_BYTES per GPU).  Calls that can overlap on one GPU race."""
+    B, Hq = _read_shapes(cache, q, block_table, seq_lens, t_k_inv_t, out)
+    _dev(q, "q"); _dev(block_table, "block_table", torch.int32); _dev(seq_lens, "seq_lens", torch.int32)
+    _dev(t_k_inv_t, "t_k_inv_t", torch.float32); _dev(out, "out", torch.float32)
+    if sm_scale is None:
+        sm_scale = 1.0 / math.sqrt(HEAD_DIM)
+    d = cache.desc()
+    check(load().kvq_decode_attn_noalloc(C.byref(d), _ptr(q), _DTYPES[q.dtype], B, Hq, _ptr(t_k_inv_t),
+                                         _ptr(block_table), block_table.shape[1], _ptr(seq_lens), max_seq_len,
+                                         float(sm_scale), _ptr(out), _stream(stream)))
+    return out
+
+
 def kvq_decode_step(cache: KVCache, q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor,
                     new_slots: torch.Tensor, block_table: torch.Tensor, seq_lens: torch.Tensor,
                     max_seq_len: int, t_k: torch.Tensor | None = None,

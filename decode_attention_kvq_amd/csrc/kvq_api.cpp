@@ -225,6 +225,39 @@ kvq_status kvq_decode_attn(const kvq_cache_desc* cache, const void* q, kvq_dtype
                                        static_cast<hipStream_t>(stream)));
 }
 
+kvq_status kvq_decode_attn_noalloc(const kvq_cache_desc* cache, const void* q, kvq_dtype q_dtype,
+                                   int32_t batch, int32_t num_q_heads, const float* t_k_inv_t,
+                                   const int32_t* block_table, int32_t max_pages, const int32_t* seq_lens,
+                                   int32_t max_seq_len, float sm_scale, float* out, void* stream) {
+  g_last_error.clear();
+  const size_t need = kvq_decode_workspace_bytes(cache, batch, num_q_heads, max_seq_len);
+  if (need > kvq::kNoAllocScratchBytes) {
+    char msg[200];
+    std::snprintf(msg, sizeof msg, "these sizes need %zu bytes of partial outputs; the allocation-free "
+                  "decode holds %zu (KVQ_NOALLOC_SCRATCH_BYTES)", need, kvq::kNoAllocScratchBytes);
+    return fail(KVQ_ERR_WORKSPACE, msg);
+  }
+  void* scratch = nullptr;
+  if (need > 0) {
+    // the scratch address is the current device's: the stream must belong to it
+    int cur = 0;
+    kvq_status s = hip_status(hipGetDevice(&cur));
+    if (s != KVQ_OK) return s;
+    if (stream) {
+      hipDevice_t sd = 0;
+      if ((s = hip_status(hipStreamGetDevice(static_cast<hipStream_t>(stream), &sd))) != KVQ_OK) return s;
+      if (sd != cur) return fail(KVQ_ERR_INVALID_ARG, "stream belongs to another device than the current one");
+    }
+    if ((s = hip_status(kvq::decode_scratch(&scratch))) != KVQ_OK) return s;
+  }
+  kvq::DecodeParams p;
+  kvq_status s = decode_params(cache, q, q_dtype, batch, num_q_heads, t_k_inv_t, block_table, max_pages, seq_lens,
+                               max_seq_len, sm_scale, out, scratch, scratch ? kvq::kNoAllocScratchBytes : 0, &p);
+  if (s != KVQ_OK || batch == 0) return s;
+  return hip_status(kvq::launch_decode(p, cache->bits_k, cache->bits_v, (int)q_dtype,
+                                       static_cast<hipStream_t>(stream)));
+}
+
 kvq_status kvq_decode_step(const kvq_cache_desc* cache, const void* q, const void* k_new, const void* v_new,
                            kvq_dtype dtype, int32_t batch, int32_t num_q_heads, const int64_t* new_slots,
                            const void* t_k, kvq_dtype t_dtype, const float* t_k_inv_t,

@@ -40,6 +40,7 @@
 // the P.V product for column n: no data moves between lanes.  Each column keeps its
 // own running max, so the only cross-lane steps per page are over the four lane groups
 // of a column; columns of one head are merged once at the end.
+#include <atomic>
 #include <type_traits>
 
 #include "kvq_device.h"
@@ -870,6 +871,34 @@ hipError_t launch_bits(const DecodeParams& p, int q_dtype, hipStream_t stream) {
 }  // namespace
 
 int decode_group_pad(int group) { return group <= 4 ? 4 : (group <= 8 ? 8 : 16); }
+
+// ---------------------------------------------------------------------------------
+// Scratch of the allocation-free decode.  Host code never passes the array's name to a
+// kernel (on the host it only stands in for the symbol): the device address comes from
+// hipGetSymbolAddress, once per device, with that device current, and is kept per device.
+// ---------------------------------------------------------------------------------
+static __device__ __align__(256) uint8_t scratch[kNoAllocScratchBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch_ptr[kMaxDevices];
+}  // namespace
+
+hipError_t decode_scratch(void** ptr) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (!p) {
+    // concurrent first calls look up the same address; either store is right
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    g_scratch_ptr[dev].store(p, std::memory_order_release);
+  }
+  *ptr = p;
+  return hipSuccess;
+}
 
 DecodeSplit decode_split(int batch, int heads_kv, int max_seq_len) {
   const int pages = (max_seq_len + kPageTokens - 1) / kPageTokens;

@@ -151,4 +151,10 @@ struct DecodeSplit {
 DecodeSplit decode_split(int batch, int heads_kv, int max_seq_len);
 int decode_group_pad(int group);
 
+// The allocation-free decode's partial outputs: a file-scope device array of this many bytes
+// on every GPU the library runs on.  decode_scratch returns its address on the current
+// device (looked up once per device).
+constexpr size_t kNoAllocScratchBytes = size_t(32) << 20;
+hipError_t decode_scratch(void** ptr);
+
 }  // namespace kvq

@@ -151,6 +151,24 @@ kvq_status kvq_decode_attn(const kvq_cache_desc* cache, const void* q, kvq_dtype
                            float* out, void* workspace, size_t workspace_bytes,
                            void* stream);
 
+/* Allocation-free kvq_decode_attn, for callers that cannot allocate device memory: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid allocation.  Arguments
+ * and results are those of kvq_decode_attn without the workspace.  The partial outputs of
+ * sequences split over several workgroups go to a device array of KVQ_NOALLOC_SCRATCH_BYTES
+ * that the library holds on every GPU it runs on, until the process ends; the call makes
+ * no allocation.  Sizes for which kvq_decode_workspace_bytes() exceeds it return
+ * KVQ_ERR_WORKSPACE before anything is enqueued.  The call runs on the current device and
+ * `stream` must belong to it (KVQ_ERR_INVALID_ARG otherwise).  Every call on one GPU shares
+ * that GPU's array, which keeps the last call's contents (nothing needs clearing: every
+ * partial is written before it is read): calls that can overlap on one GPU (streams with no
+ * ordering between them) race, and must not be made. */
+enum { KVQ_NOALLOC_SCRATCH_BYTES = 32 << 20 };
+kvq_status kvq_decode_attn_noalloc(const kvq_cache_desc* cache, const void* q, kvq_dtype q_dtype,
+                                   int32_t batch, int32_t num_q_heads, const float* t_k_inv_t,
+                                   const int32_t* block_table, int32_t max_pages,
+                                   const int32_t* seq_lens, int32_t max_seq_len, float sm_scale,
+                                   float* out, void* stream);
+
 /* One decode step with the step's new tokens: for every sequence b, the key and value of
  * its new token (all KV heads) are encoded exactly as kvq_quantize_append encodes them and
  * written at new_slots[b]; then sequence b is read as by kvq_decode_attn over positions

@@ -233,3 +233,15 @@ def test_window_argument_checks(lib):
     assert prefill(w=_win(flush=0)) == -1
     assert prefill(n=0) == 0
     assert prefill(B=0) == 0
+
+
+def test_noalloc_rejects_sizes_beyond_its_scratch(lib):
+    """Sizes whose partial outputs exceed the allocation-free decode's array are refused on
+    the host, before any device call (null pointers are never touched)."""
+    d = _lib.KvqCacheDesc(8, 128, 64, 2, 2, 0, 0, 0.01, 0.99, 2.83, 2.83, 2048, None, None)
+    need = lib.kvq_decode_workspace_bytes(C.byref(d), 65535, 128, 131072)
+    assert need > _lib.NOALLOC_SCRATCH_BYTES
+    st = lib.kvq_decode_attn_noalloc(C.byref(d), None, 1, 65535, 128, None, None, 2048, None, 131072,
+                                     0.088, None, None)
+    assert st == -3, st
+    assert b"allocation-free" in lib.kvq_last_error()
