@@ -320,6 +320,17 @@ def step_traffic_bytes():
     return float(fields["traffic_bytes"])
 
 
+def cpu_model() -> str:
+    """The host CPU's model name, from /proc/cpuinfo."""
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(w, seconds):
     """The oracle's decode attention on whole sequences of the workload's shape (random
     packed codes: the oracle's cost does not depend on the values), unmodified: first on one
@@ -348,13 +359,16 @@ def cpu_baseline(w, seconds):
     t0 = time.perf_counter()
     n1 = run(t0 + seconds / 3)
     el1 = time.perf_counter() - t0
-    cores = max(1, min(16, len(os.sched_getaffinity(0))))
+    avail = len(os.sched_getaffinity(0))
+    cores = max(1, min(16, avail))           # one GPU's share of a shared host: 16 threads
     t0 = time.perf_counter()
     with cf.ThreadPoolExecutor(max_workers=cores) as ex:
         counts = list(ex.map(run, [t0 + seconds * 2 / 3] * cores))
     el = time.perf_counter() - t0
     done = sum(counts)
     return {"value": done * w.seq_len / el, "unit": "cached tokens/s", "cores": cores, "kind": "oracle",
+            "cpu_model": cpu_model(), "nproc": os.cpu_count(), "affinity_cpus": avail,
+            "thread_cap": "16 threads at most (the host share of one GPU)",
             "single_thread_value": n1 * w.seq_len / el1,
             "sample": f"whole sequences of {w.seq_len} tokens x {w.heads_q} query heads (one decode step "
                       f"each): {done} on {cores} threads in {el:.1f} s; {n1} on one thread in {el1:.1f} s"}

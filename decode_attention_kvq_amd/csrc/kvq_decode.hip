@@ -55,6 +55,10 @@ constexpr int kThreads = 64 * kWaves;
 // not latency), and two leave room for a three-page register ring.
 constexpr int kWavesPerSimd = 2;
 constexpr int kResidentWaves = 256 * 4 * kWavesPerSimd;
+#ifndef KVQ_MIN_PAGES_PER_WAVE
+#define KVQ_MIN_PAGES_PER_WAVE 4
+#endif
+constexpr int kMinPagesPerWave = KVQ_MIN_PAGES_PER_WAVE;
 
 typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
@@ -157,24 +161,24 @@ __device__ __forceinline__ f32x4 mma_fp4_fp6(int opsel, const v8i& a, const v8i&
   }
 }
 
-// fp6 e2m3 (1 sign, 2 exponent bits with bias 1, 3 fraction bits; largest 7.5), round to
-// nearest even, for |v| <= 7.5.
-__device__ __forceinline__ uint32_t e2m3_encode(float v) {
-  const float a = fabsf(v);
-  uint32_t mag;
-  if (a < 1.0f) {
-    mag = (uint32_t)rintf(a * 8.0f);                       // 8 encodes 1.0 (exponent 1)
-  } else {
-    const int e = ilogbf(a);                               // 0, 1 or 2
-    mag = (uint32_t)((e + 1) * 8) + (uint32_t)rintf((ldexpf(a, -e) - 1.0f) * 8.0f);
-  }
-  mag = mag > 31u ? 31u : mag;
-  return (v < 0.0f ? 32u : 0u) | mag;
+typedef uint32_t u32x6 __attribute__((ext_vector_type(6)));
+// 32 fp32 values to packed fp6 e2m3 (1 sign, 2 exponent bits with bias 1, 3 fraction bits;
+// largest 7.5): element 2i of the result (bits 12i .. 12i+5) is a[i] / 2^e, element 2i + 1 is
+// b[i] / 2^e, where 2^e is the power of two of `scale`; round to nearest even, saturating
+// (checked on the GPU).  Written as inline assembly with an early-clobber result: the
+// compiler's builtin for this instruction let the result overlap the second source, which
+// the instruction overwrites before reading it.
+__device__ __forceinline__ u32x6 fp6_pack32(f32x16 a, f32x16 b, float scale) {
+  u32x6 d;
+  asm("v_cvt_scalef32_2xpk16_fp6_f32 %0, %1, %2, %3" : "=&v"(d) : "v"(a), "v"(b), "v"(scale));
+  return d;
 }
-__device__ __forceinline__ float e2m3_decode(uint32_t c) {
-  const uint32_t mag = c & 31u, e = mag >> 3, m = mag & 7u;
-  const float a = e == 0 ? (float)m * 0.125f : ldexpf(1.0f + (float)m * 0.125f, (int)e - 1);
-  return (c & 32u) ? -a : a;
+// The inverse at unit scale: element j of the packed fp6 values as fp16 (exact).
+typedef _Float16 half32 __attribute__((ext_vector_type(32)));
+__device__ __forceinline__ half32 fp6_unpack32_f16(u32x6 c) {
+  half32 d;
+  asm("v_cvt_scalef32_pk32_f16_fp6 %0, %1, %2" : "=&v"(d) : "v"(c), "v"(1.0f));
+  return d;
 }
 
 // ---------------------------------------------------------------------------------
@@ -278,9 +282,8 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
 
   // merge buffers (per wave: 16 columns x 128 channels, then 16 x (m, l))
   __shared__ __attribute__((aligned(16))) uint8_t smem[kWaves * 16 * (kHeadDim + 2) * 4];
-  // prologue scratch: q, then q'; per head the sum of q' as carried by kQBase and kQTerms terms
+  // prologue scratch: q, then q'
   __shared__ __attribute__((aligned(16))) float qs[GP * kHeadDim];
-  __shared__ float hconst[GP * 2];
 
   // ---- this wave's pages ----
   // with full-precision windows the cache holds the quantized middle positions only
@@ -389,84 +392,64 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
       }
   }
   lds_barrier();
-  // q' as fp6 terms t_k with scales 2^(e1 - 4k), e1 per head so that max|q'| 2^-e1 <= 7.5;
-  // each term holds the previous remainder to within a quarter of its scale.  The product
+  // q' as fp6 (e2m3) terms t_k with scales 2^(e1 - 4k), e1 per head so that
+  // max|q'| 2^-e1 <= 7.5; each term holds the previous remainder to within a quarter of its
+  // scale.  Every lane builds its own operand, the channels key_channel(kg, j) of head gq,
+  // with the fp6 packing conversion, and converts it back for the remainder.  The product
   // with the fp4 codes (value c/2) gives half of q'.code: F = 2.
   v8i bq6[kQTerms];
   int sreg[kQTerms];
   const int gq = n % GP;
-  uint8_t* qcode = smem;                                           // [term][head][channel]
-  uint32_t* qpack = reinterpret_cast<uint32_t*>(smem + kQTerms * GP * kHeadDim);  // [term][kg][head][6]
-  int* qexp = reinterpret_cast<int*>(qpack + kQTerms * 4 * GP * 6);
-  // fp6 operand and scale register of term k for this lane
-  auto term_operand = [&](int k, v8i& bq, int& sr) {
-#pragma unroll
-    for (int d = 0; d < 6; ++d) bq[d] = (int)qpack[((k * 4 + kg) * GP + gq) * 6 + d];
-    bq[6] = 0;
-    bq[7] = 0;
-    // scale byte t (selected per tile by op_sel): the term's scale for this lane's column
-    // block, 2^-127 (contributes nothing) for the others
-    uint32_t sc = 0;
-#pragma unroll
-    for (int t = 0; t < NB; ++t) sc |= (beta == t ? (uint32_t)(127 + qexp[gq] - 4 * k) : 0u) << (8 * t);
-    sr = (int)sc;
-  };
-  {
-    for (int g = wave; g < GP; g += kWaves) {
-      const float a0 = g < G ? qs[g * kHeadDim + lane] : 0.0f, a1 = g < G ? qs[g * kHeadDim + lane + 64] : 0.0f;
-      float amax = fmaxf(fabsf(a0), fabsf(a1));
-#pragma unroll
-      for (int d = 1; d < 64; d <<= 1) amax = fmaxf(amax, __shfl_xor(amax, d));
-      int e1 = 0;
-      if (amax > 0.0f) {
-        const int E = ilogbf(amax);
-        e1 = ldexpf(amax, 2 - E) <= 7.5f ? E - 2 : E - 1;
-      }
-      e1 = max(e1, -126 + 4 * (kQTerms - 1));   // the last term's scale stays a normal E8M0 value
-      float r0 = a0, r1 = a1, qsum3 = 0.0f, qsum4 = 0.0f;
-#pragma unroll
-      for (int k = 0; k < kQTerms; ++k) {
-        const int e = e1 - 4 * k;
-        const uint32_t c0 = e2m3_encode(ldexpf(r0, -e)), c1 = e2m3_encode(ldexpf(r1, -e));
-        const float v0 = ldexpf(e2m3_decode(c0), e), v1 = ldexpf(e2m3_decode(c1), e);
-        r0 -= v0;
-        r1 -= v1;
-        if (k < kQBase) qsum3 += v0 + v1;
-        qsum4 += v0 + v1;
-        qcode[(k * GP + g) * kHeadDim + lane] = (uint8_t)c0;
-        qcode[(k * GP + g) * kHeadDim + lane + 64] = (uint8_t)c1;
-      }
-#pragma unroll
-      for (int d = 1; d < 64; d <<= 1) {
-        qsum3 += __shfl_xor(qsum3, d);
-        qsum4 += __shfl_xor(qsum4, d);
-      }
-      if (lane == 0) {
-        hconst[2 * g] = qsum3;
-        hconst[2 * g + 1] = qsum4;
-        qexp[g] = e1;
-      }
-    }
-    lds_barrier();
-    // operand words: element j of lane group kg at bits 6j .. 6j+5 of six dwords
-    for (int it = threadIdx.x; it < kQTerms * 4 * GP * 6; it += kThreads) {
-      const int d = it % 6, g = (it / 6) % GP, kgi = (it / (6 * GP)) % 4, k = it / (24 * GP);
-      const uint8_t* src = qcode + (k * GP + g) * kHeadDim;
-      uint32_t word = 0;
-      const int j0 = (32 * d) / 6, j1 = min(31, (32 * d + 31) / 6);
-      for (int j = j0; j <= j1; ++j) {
-        const uint32_t c = src[key_channel<BK>(kgi, j)];
-        const int sh = 6 * j - 32 * d;
-        word |= sh >= 0 ? c << sh : c >> (-sh);
-      }
-      qpack[it] = word;
-    }
-    lds_barrier();
-#pragma unroll
-    for (int k = 0; k < kQTerms; ++k) term_operand(k, bq6[k], sreg[k]);
-  }
   constexpr float F = 2.0f;                                              // score = F * x'
-  const float qsf3 = gq < G ? hconst[2 * gq] / F : 0.0f;
+  float qsf3, qsf4;                      // sum(q') as carried by kQBase and kQTerms terms, / F
+  {
+    // a[i], b[i]: channels key_channel(kg, 2i), key_channel(kg, 2i + 1) (the packing puts
+    // a[i] at element 2i and b[i] at 2i + 1), then the remainders
+    f32x16 a, b;
+    const float* qh = qs + gq * kHeadDim + 32 * kg;
+    float amax = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      a[i] = qh[key_channel<BK>(0, 2 * i)];
+      b[i] = qh[key_channel<BK>(0, 2 * i + 1)];
+      amax = fmaxf(amax, fmaxf(fabsf(a[i]), fabsf(b[i])));
+    }
+    amax = col_max(amax);                  // over the four lane groups: the whole head
+    int e1 = 0;
+    if (amax > 0.0f) {
+      const int E = ilogbf(amax);
+      e1 = ldexpf(amax, 2 - E) <= 7.5f ? E - 2 : E - 1;
+    }
+    e1 = max(e1, -126 + 4 * (kQTerms - 1));   // the last term's scale stays a normal E8M0 value
+    float s3 = 0.0f, s4 = 0.0f;
+#pragma unroll
+    for (int k = 0; k < kQTerms; ++k) {
+      const float scale = ldexpf(1.0f, e1 - 4 * k);
+      const u32x6 code = fp6_pack32(a, b, scale);
+      const half32 h = fp6_unpack32_f16(code);          // the term's values / scale (exact)
+      float hs = 0.0f;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        a[i] = __builtin_fmaf(-(float)h[2 * i], scale, a[i]);
+        b[i] = __builtin_fmaf(-(float)h[2 * i + 1], scale, b[i]);
+        hs += (float)h[2 * i] + (float)h[2 * i + 1];    // exact: multiples of 1/8 below 2^9
+      }
+      if (k < kQBase) s3 += hs * scale;
+      s4 += hs * scale;
+#pragma unroll
+      for (int d = 0; d < 6; ++d) bq6[k][d] = (int)code[d];
+      bq6[k][6] = 0;
+      bq6[k][7] = 0;
+      // scale byte t (selected per tile by op_sel): the term's scale for this lane's column
+      // block, 2^-127 (contributes nothing) for the others
+      uint32_t sc = 0;
+#pragma unroll
+      for (int t = 0; t < NB; ++t) sc |= (beta == t ? (uint32_t)(127 + e1 - 4 * k) : 0u) << (8 * t);
+      sreg[k] = (int)sc;
+    }
+    qsf3 = gq < G ? col_sum(s3) / F : 0.0f;
+    qsf4 = gq < G ? col_sum(s4) / F : 0.0f;
+  }
 
 
   // per (accumulator a, row r): token u = 4*(a*NB + beta) + r of this lane group
@@ -591,7 +574,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
     if (__any(fabsf(mx) > kBigScore / F)) {
 #pragma unroll
       for (int t4 = 0; t4 < 4; ++t4) key_products(t4, integral_constant<int, kQBase>{}, integral_constant<int, 1>{});
-      mx = token_scores(gq < G ? hconst[2 * gq + 1] / F : 0.0f);
+      mx = token_scores(qsf4);
     }
     u32x2 svp[A], zvp[A];
 #pragma unroll
@@ -825,21 +808,37 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
   }
 }
 
+// Log-sum-exp merge of the chunks of one (sequence, query head) row: thread = channel.
+// The chunks' (max, sum) pairs are staged in LDS 64 at a time by the whole block, and each
+// thread's partial outputs are read with several loads in flight, so the merge costs a few
+// memory round trips rather than one per chunk.  Blocks of chunks merge online.
+constexpr int kCombineBlock = 64;
 __global__ __launch_bounds__(128) void combine_kernel(DecodeParams p) {
+  __shared__ float sml[2 * kCombineBlock];
   const int64_t row = blockIdx.x;        // b * Hq + hq
   const int ch = threadIdx.x;
   const float* ml = p.ws_ml + row * p.chunks * 2;
-  float M = -__builtin_inff();
-  for (int c = 0; c < p.chunks; ++c) M = fmaxf(M, ml[2 * c]);
-  float L = 0.0f, O = 0.0f;
-  if (M != -__builtin_inff()) {
-    for (int c = 0; c < p.chunks; ++c) {
-      const float mc = ml[2 * c];
-      if (mc != -__builtin_inff()) {
-        const float f = exp2f(mc - M);
-        L = __builtin_fmaf(ml[2 * c + 1], f, L);
-        O = __builtin_fmaf(p.ws_o[(row * p.chunks + c) * kHeadDim + ch], f, O);
-      }
+  const float* po = p.ws_o + row * p.chunks * kHeadDim + ch;
+  float M = -__builtin_inff(), L = 0.0f, O = 0.0f;
+  for (int c0 = 0; c0 < p.chunks; c0 += kCombineBlock) {
+    const int nc = min(kCombineBlock, p.chunks - c0);
+    __syncthreads();
+    if (ch < 2 * nc) sml[ch] = ml[2 * c0 + ch];
+    __syncthreads();
+    float Mb = -__builtin_inff();
+    for (int c = 0; c < nc; ++c) Mb = fmaxf(Mb, sml[2 * c]);
+    if (Mb == -__builtin_inff()) continue;           // no tokens in these chunks
+    const float Mn = fmaxf(M, Mb);
+    const float r = M == -__builtin_inff() ? 0.0f : exp2f(M - Mn);
+    L *= r;
+    O *= r;
+    M = Mn;
+#pragma unroll 8
+    for (int c = 0; c < nc; ++c) {
+      const float mc = sml[2 * c];
+      const float f = mc == -__builtin_inff() ? 0.0f : exp2f(mc - M);
+      L = __builtin_fmaf(sml[2 * c + 1], f, L);
+      O = __builtin_fmaf(po[(int64_t)(c0 + c) * kHeadDim], f, O);
     }
   }
   p.out[row * kHeadDim + ch] = L > 0.0f ? O / L : 0.0f;
@@ -903,10 +902,10 @@ hipError_t decode_scratch(void** ptr) {
 DecodeSplit decode_split(int batch, int heads_kv, int max_seq_len) {
   const int pages = (max_seq_len + kPageTokens - 1) / kPageTokens;
   const int64_t units = (int64_t)batch * heads_kv;
-  // about kResidentWaves waves (one resident round), 4 to 64 pages per wave
+  // about kResidentWaves waves (one resident round), kMinPagesPerWave to 64 pages per wave
   // (a wave's page ids fit one register, one per lane)
   int64_t ppw = (units * pages + kResidentWaves - 1) / kResidentWaves;
-  if (ppw < 4) ppw = 4;
+  if (ppw < kMinPagesPerWave) ppw = kMinPagesPerWave;
   if (ppw > 64) ppw = 64;
   const int64_t waves = pages > 0 ? (pages + ppw - 1) / ppw : 1;
   DecodeSplit s;
