@@ -490,7 +490,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
   }
   float m = -__builtin_inff();   // running max of x' for this lane's column
   int S = 30;                    // P~ carries 2^(S - vcls)
-  int hmax = -128;               // exponent of the largest P~ accumulated so far (units of S)
+  int hmax = -128;               // exponent of the lane's largest P~ accumulated so far (units of S)
 
   // ---- page walk: compute page i from ring slot i % PIPE, then refill the slot ----
   auto compute = [&](const PageRegs<BK, BV, A>& pr, int i) {
@@ -542,6 +542,13 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
     // scales and zeros enter the arithmetic as fp16 operands of mixed fma (no conversions).
     // score = s_k * (q' . code) + z_k * sum(q'), with sum(q') as the terms carry it
     float x[A][4];
+    u32x2 svp[A], zvp[A];
+#pragma unroll
+    for (int a = 0; a < A; ++a) {
+      svp[a] = pr.meta[a][2];
+      zvp[a] = pr.meta[a][3];
+    }
+    // the lane's largest score (the column's max is reduced only where it is needed)
     auto token_scores = [&](float qsf) {
 #pragma unroll
       for (int a = 0; a < A; ++a) {
@@ -555,52 +562,45 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
           x[a][r] = __builtin_fmaf(sacc[a][r], (float)sk[r], zq);
         }
       }
-      if (partial) {                        // absent tokens: no weight
+      if (partial) {                        // absent tokens: no weight, no garbage scale
 #pragma unroll
         for (int a = 0; a < A; ++a)
 #pragma unroll
-          for (int r = 0; r < 4; ++r)
-            x[a][r] = 16 * kg + 4 * (a * NB + beta) + r < valid_tokens ? x[a][r] : -__builtin_inff();
+          for (int r = 0; r < 4; ++r) {
+            const bool ok = 16 * kg + 4 * (a * NB + beta) + r < valid_tokens;
+            x[a][r] = ok ? x[a][r] : -__builtin_inff();
+            const uint32_t keep = ok ? 0xFFFFFFFFu : ((r & 1) ? 0x0000FFFFu : 0xFFFF0000u);
+            svp[a][r >> 1] &= keep;
+            zvp[a][r >> 1] &= keep;
+          }
       }
       float mx = x[0][0];
 #pragma unroll
       for (int a = 0; a < A; ++a)
 #pragma unroll
         for (int r = 0; r < 4; ++r) mx = fmaxf(mx, x[a][r]);
-      return col_max(mx);
+      return mx;
     };
     float mx = token_scores(qsf3);
-    // (a column without tokens in a partial page has mx = -inf and takes the branch too)
+    // Large scores take a fourth q' term: a column whose max |score| passes kBigScore / F
+    // has a lane whose own max does too (the column max is one of the lanes' maxima, and
+    // when it is below -kBigScore / F every lane's is).  A lane without tokens in a partial
+    // page has mx = -inf and takes the branch too.
     if (__any(fabsf(mx) > kBigScore / F)) {
 #pragma unroll
       for (int t4 = 0; t4 < 4; ++t4) key_products(t4, integral_constant<int, kQBase>{}, integral_constant<int, 1>{});
       mx = token_scores(qsf4);
-    }
-    u32x2 svp[A], zvp[A];
-#pragma unroll
-    for (int a = 0; a < A; ++a) {
-      svp[a] = pr.meta[a][2];
-      zvp[a] = pr.meta[a][3];
-    }
-    if (partial) {                          // absent tokens: no weight, no garbage scale
-#pragma unroll
-      for (int a = 0; a < A; ++a)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const bool ok = 16 * kg + 4 * (a * NB + beta) + r < valid_tokens;
-          const uint32_t keep = ok ? 0xFFFFFFFFu : ((r & 1) ? 0x0000FFFFu : 0xFFFF0000u);
-          svp[a][r >> 1] &= keep;
-          zvp[a][r >> 1] &= keep;
-        }
     }
     // ---- online softmax, per column ----
     // Lazy maximum: the reference max m of a column moves only when the page's scores
     // exceed it by more than kLag (log2 units), so p = 2^(F(x - m)) <= 2^kLag.  Rescaling
     // is wave-uniform, so an eager rule would run it whenever any of the 16 columns grows.
     constexpr float kLag = 8.0f;
-    const bool need_m = F * (mx - m) > kLag;       // false when the column has no token here
-    if (__any(need_m)) {
-      const float m_new = need_m ? mx : m;
+    // a column's max passes m + kLag / F exactly when one of its lanes' maxima does
+    if (__any(F * (mx - m) > kLag)) {
+      const float mxc = col_max(mx);
+      const bool need_m = F * (mxc - m) > kLag;   // false when the column has no token here
+      const float m_new = need_m ? mxc : m;
       const float alpha = exp2f(F * (m - m_new));
 #pragma unroll
       for (int mt = 0; mt < 8; ++mt) acc_o[mt] *= alpha;
@@ -640,27 +640,39 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
     constexpr int kPtTarget = kPtHi - (int)kLag - 2;
     constexpr int kPtLo = kPtTarget - 8;
     constexpr int kStateMax = 48;
-    const int pcol = col_max_i((int)pbits);
-    const int e = (pcol >> 23) - 127;                 // exponent of the largest P~ (pcol > 0)
-    const bool need_s = pcol != 0 && (e > kPtHi || e < kPtLo);
-    if (__any(need_s)) {
-      const int d = need_s ? min(kPtTarget - e, kStateMax - hmax) : 0;
-      const float f = __builtin_amdgcn_ldexpf(1.0f, d);
+    // The column's largest P~ leaves the range above when one of its lanes' largest does,
+    // and below when every lane of the column that holds weight is below it: a vote of the
+    // lanes (column n owns lanes n, n + 16, n + 32, n + 48) decides whether the column's
+    // largest is needed at all.  hmax is kept per lane; the column's is the largest of its
+    // lanes'.
+    const int el = (int)(pbits >> 23) - 127;          // the lane's largest P~ exponent (pbits > 0)
+    const uint64_t held = __ballot(pbits != 0u);
+    const uint64_t in_range = __ballot(pbits != 0u && el >= kPtLo);
+    auto fold = [](uint64_t v) -> uint32_t { v |= v >> 32; v |= v >> 16; return (uint32_t)v & 0xFFFFu; };
+    if (__any(pbits != 0u && el > kPtHi) || (fold(held) & ~fold(in_range)) != 0u) {
+      const int pcol = col_max_i((int)pbits);
+      const int e = (pcol >> 23) - 127;               // exponent of the largest P~ (pcol > 0)
+      const bool need_s = pcol != 0 && (e > kPtHi || e < kPtLo);
+      if (__any(need_s)) {
+        const int hcol = col_max_i(hmax);               // (lane exchanges stay outside divergent code)
+        const int d = need_s ? min(kPtTarget - e, kStateMax - hcol) : 0;
+        const float f = __builtin_amdgcn_ldexpf(1.0f, d);
 #pragma unroll
-      for (int mt = 0; mt < 8; ++mt) acc_o[mt] *= f;
+        for (int mt = 0; mt < 8; ++mt) acc_o[mt] *= f;
 #pragma unroll
-      for (int a = 0; a < A; ++a)
+        for (int a = 0; a < A; ++a)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          lsum[a][r] *= f;
-          zacc[a][r] *= f;
-          pt[a][r] *= f;
-          nb[a][r] += (float)d;
-        }
-      S += d;
-      hmax += d;
+          for (int r = 0; r < 4; ++r) {
+            lsum[a][r] *= f;
+            zacc[a][r] *= f;
+            pt[a][r] *= f;
+            nb[a][r] += (float)d;
+          }
+        S += d;
+        hmax += d;
+      }
     }
-    hmax = max(hmax, pcol != 0 ? e : -128);
+    hmax = max(hmax, pbits != 0u ? el : -128);
 
     // ---- P.V: B operand element (s, 2*jj + h) is token u = v_token(s, 2jj+h), i.e. tile
     // b(s, h) = u/4, row jj; the lane feeds only its own tiles, the rest of the operand is 0
