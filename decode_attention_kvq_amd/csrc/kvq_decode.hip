@@ -280,10 +280,13 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
   const int beta = n / GP;           // column block of this lane
   const int G = p.group;
 
-  // merge buffers (per wave: 16 columns x 128 channels, then 16 x (m, l))
-  __shared__ __attribute__((aligned(16))) uint8_t smem[kWaves * 16 * (kHeadDim + 2) * 4];
-  // prologue scratch: q, then q'
-  __shared__ __attribute__((aligned(16))) float qs[GP * kHeadDim];
+  // merge buffers (per wave: 16 columns x 128 channels in rows of kHeadDim + 1, so that the
+  // scattered writes of a half wave reach 32 banks; then 16 x (m, l))
+  __shared__ __attribute__((aligned(16))) uint8_t smem[kWaves * 16 * (kHeadDim + 3) * 4];
+  // prologue scratch: q (rows of kHeadDim), then q' (rows of kQRow: each 32-channel group in
+  // 33 floats, so that the 16 (head, group) operands read at once hit distinct banks)
+  constexpr int kQRow = 4 * 33;
+  __shared__ __attribute__((aligned(16))) float qs[GP * kQRow];
 
   // ---- this wave's pages ----
   // with full-precision windows the cache holds the quantized middle positions only
@@ -380,16 +383,11 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
   }
   lds_barrier();                           // every read of q is done: q' replaces it
   if (tw && cgrp == 0) {
+    // channels j0 .. j0 + 3 sit in group j0 / 32 = wave; heads past G read as 0
 #pragma unroll
     for (int g = 0; g < GP; ++g)
-      if (g < G) {
-        float4 o;
-        o.x = qacc[g][0] * p.score_scale;
-        o.y = qacc[g][1] * p.score_scale;
-        o.z = qacc[g][2] * p.score_scale;
-        o.w = qacc[g][3] * p.score_scale;
-        *reinterpret_cast<float4*>(qs + g * kHeadDim + j0) = o;
-      }
+#pragma unroll
+      for (int k = 0; k < 4; ++k) qs[g * kQRow + 33 * wave + 4 * quad + k] = g < G ? qacc[g][k] * p.score_scale : 0.0f;
   }
   lds_barrier();
   // q' as fp6 (e2m3) terms t_k with scales 2^(e1 - 4k), e1 per head so that
@@ -406,7 +404,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
     // a[i], b[i]: channels key_channel(kg, 2i), key_channel(kg, 2i + 1) (the packing puts
     // a[i] at element 2i and b[i] at 2i + 1), then the remainders
     f32x16 a, b;
-    const float* qh = qs + gq * kHeadDim + 32 * kg;
+    const float* qh = qs + gq * kQRow + 33 * kg;
     float amax = 0.0f;
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
@@ -767,8 +765,8 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
   const float mlog2 = any_page ? F * m : -__builtin_inff();
   const float oscale = ldexpf(1.0f, 24 - S);
   __syncthreads();
-  float (*red_o)[16][kHeadDim] = reinterpret_cast<float (*)[16][kHeadDim]>(smem);
-  float (*red_ml)[16][2] = reinterpret_cast<float (*)[16][2]>(smem + kWaves * 16 * kHeadDim * 4);
+  float (*red_o)[16][kHeadDim + 1] = reinterpret_cast<float (*)[16][kHeadDim + 1]>(smem);
+  float (*red_ml)[16][2] = reinterpret_cast<float (*)[16][2]>(smem + kWaves * 16 * (kHeadDim + 1) * 4);
 #pragma unroll
   for (int mt = 0; mt < 8; ++mt)
 #pragma unroll
