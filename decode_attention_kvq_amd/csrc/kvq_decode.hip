@@ -784,25 +784,32 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
   const int hq0 = kvh * G;
   for (int idx = threadIdx.x; idx < G * kHeadDim; idx += kThreads) {
     const int gg = idx / kHeadDim, ch = idx % kHeadDim;
-    float M = -__builtin_inff();
+    // every read first, with no branch between them, so that they are all in flight at once
+    constexpr int NP = kWaves * NB;
+    float mw[NP], lw[NP], ow[NP];
 #pragma unroll
     for (int w = 0; w < kWaves; ++w)
 #pragma unroll
-      for (int bb = 0; bb < NB; ++bb) M = fmaxf(M, red_ml[w][bb * GP + gg][0]);
+      for (int bb = 0; bb < NB; ++bb) {
+        const int col = bb * GP + gg;
+        mw[w * NB + bb] = red_ml[w][col][0];
+        lw[w * NB + bb] = red_ml[w][col][1];
+        ow[w * NB + bb] = red_o[w][col][ch];
+      }
+    float M = -__builtin_inff();
+#pragma unroll
+    for (int k = 0; k < NP; ++k) M = fmaxf(M, mw[k]);
+    // a part without tokens (m = -inf) is left out by a select: its other fields are not
+    // meaningful (its softmax state never had a finite maximum); a head without any token
+    // (M = -inf) keeps L = O = 0
+    const float Mf = M == -__builtin_inff() ? 0.0f : M;
     float L = 0.0f, O = 0.0f;
-    if (M != -__builtin_inff()) {
 #pragma unroll
-      for (int w = 0; w < kWaves; ++w)
-#pragma unroll
-        for (int bb = 0; bb < NB; ++bb) {
-          const int col = bb * GP + gg;
-          const float mw = red_ml[w][col][0];
-          if (mw != -__builtin_inff()) {
-            const float f = exp2f(mw - M);
-            L = __builtin_fmaf(red_ml[w][col][1], f, L);
-            O = __builtin_fmaf(red_o[w][col][ch], f, O);
-          }
-        }
+    for (int k = 0; k < NP; ++k) {
+      const bool live = mw[k] != -__builtin_inff();
+      const float f = __builtin_amdgcn_exp2f(mw[k] - Mf);
+      L = live ? __builtin_fmaf(lw[k], f, L) : L;
+      O = live ? __builtin_fmaf(ow[k], f, O) : O;
     }
     const int hq = hq0 + gg;
     if (p.chunks == 1 && p.win.flush == 0) {
@@ -819,9 +826,9 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
 }
 
 // Log-sum-exp merge of the chunks of one (sequence, query head) row: thread = channel.
-// The chunks' (max, sum) pairs are staged in LDS 64 at a time by the whole block, and each
-// thread's partial outputs are read with several loads in flight, so the merge costs a few
-// memory round trips rather than one per chunk.  Blocks of chunks merge online.
+// Chunks go 64 at a time: each thread's partial outputs of the block are loaded first, then
+// the chunks' (max, sum) pairs are staged in LDS by the whole block, so a block costs about
+// one memory round trip.  Blocks of chunks merge online.
 constexpr int kCombineBlock = 64;
 __global__ __launch_bounds__(128) void combine_kernel(DecodeParams p) {
   __shared__ float sml[2 * kCombineBlock];
@@ -832,6 +839,15 @@ __global__ __launch_bounds__(128) void combine_kernel(DecodeParams p) {
   float M = -__builtin_inff(), L = 0.0f, O = 0.0f;
   for (int c0 = 0; c0 < p.chunks; c0 += kCombineBlock) {
     const int nc = min(kCombineBlock, p.chunks - c0);
+    // the block's partial outputs go out first (they do not depend on the maxima), in groups
+    // of 8 behind a uniform test, so that one memory round trip covers them all
+    float ov[kCombineBlock];
+#pragma unroll
+    for (int c8 = 0; c8 < kCombineBlock; c8 += 8)
+      if (c8 < nc) {
+#pragma unroll
+        for (int c = c8; c < c8 + 8; ++c) ov[c] = po[(int64_t)(c0 + min(c, nc - 1)) * kHeadDim];
+      }
     __syncthreads();
     if (ch < 2 * nc) sml[ch] = ml[2 * c0 + ch];
     __syncthreads();
@@ -839,17 +855,23 @@ __global__ __launch_bounds__(128) void combine_kernel(DecodeParams p) {
     for (int c = 0; c < nc; ++c) Mb = fmaxf(Mb, sml[2 * c]);
     if (Mb == -__builtin_inff()) continue;           // no tokens in these chunks
     const float Mn = fmaxf(M, Mb);
-    const float r = M == -__builtin_inff() ? 0.0f : exp2f(M - Mn);
+    const float r = M == -__builtin_inff() ? 0.0f : __builtin_amdgcn_exp2f(M - Mn);
     L *= r;
     O *= r;
     M = Mn;
-#pragma unroll 8
-    for (int c = 0; c < nc; ++c) {
-      const float mc = sml[2 * c];
-      const float f = mc == -__builtin_inff() ? 0.0f : exp2f(mc - M);
-      L = __builtin_fmaf(sml[2 * c + 1], f, L);
-      O = __builtin_fmaf(po[(int64_t)(c0 + c) * kHeadDim], f, O);
-    }
+    // a chunk without tokens (m = -inf) is left out by a select
+#pragma unroll
+    for (int c8 = 0; c8 < kCombineBlock; c8 += 8)
+      if (c8 < nc) {
+#pragma unroll
+        for (int c = c8; c < c8 + 8; ++c) {
+          const float mc = sml[2 * min(c, nc - 1)];
+          const bool live = c < nc && mc != -__builtin_inff();
+          const float f = __builtin_amdgcn_exp2f(mc - M);
+          L = live ? __builtin_fmaf(sml[2 * min(c, nc - 1) + 1], f, L) : L;
+          O = live ? __builtin_fmaf(ov[c], f, O) : O;
+        }
+      }
   }
   p.out[row * kHeadDim + ch] = L > 0.0f ? O / L : 0.0f;
 }
