@@ -425,13 +425,24 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
       const float scale = ldexpf(1.0f, e1 - 4 * k);
       const u32x6 code = fp6_pack32(a, b, scale);
       const half32 h = fp6_unpack32_f16(code);          // the term's values / scale (exact)
-      float hs = 0.0f;
+      if (k + 1 < kQTerms) {                            // (the last remainder is not used)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        a[i] = __builtin_fmaf(-(float)h[2 * i], scale, a[i]);
-        b[i] = __builtin_fmaf(-(float)h[2 * i + 1], scale, b[i]);
-        hs += (float)h[2 * i] + (float)h[2 * i + 1];    // exact: multiples of 1/8 below 2^9
+        for (int i = 0; i < 16; ++i) {
+          a[i] = __builtin_fmaf(-(float)h[2 * i], scale, a[i]);
+          b[i] = __builtin_fmaf(-(float)h[2 * i + 1], scale, b[i]);
+        }
       }
+      // the term's sum by a packed fp16 tree: its values are multiples of 1/8 of magnitude at
+      // most 7.5, so every partial sum is a multiple of 1/8 below 256 in magnitude, where fp16
+      // is exact (steps of 1/8 from 128 to 256)
+      half2_t hp[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) hp[i] = half2_t{h[2 * i], h[2 * i + 1]};
+#pragma unroll
+      for (int w = 8; w >= 1; w >>= 1)
+#pragma unroll
+        for (int i = 0; i < w; ++i) hp[i] = hp[i] + hp[i + w];
+      const float hs = (float)hp[0][0] + (float)hp[0][1];
       if (k < kQBase) s3 += hs * scale;
       s4 += hs * scale;
 #pragma unroll
