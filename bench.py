@@ -97,7 +97,9 @@ def setup_decode(w, torch, api, calib, synth, dev):
     # the step's new token of each sequence is appended at its last position
     knew, vnew = synth.kv_tokens_torch(w, B, dev, seq=10_000)
     new_slots = torch.tensor([b * pps * 64 + w.seq_len - 1 for b in range(B)], dtype=torch.int64, device=dev)
-    ws = torch.empty(max(1, api.decode_workspace_bytes(cache, B, w.heads_q, w.seq_len)), dtype=torch.uint8,
+    # the step's workspace: the decode's partial outputs and the query-operand image that the
+    # step's append launch builds (the plain decode uses the first part only)
+    ws = torch.empty(max(1, api.decode_step_workspace_bytes(cache, B, w.heads_q, w.seq_len)), dtype=torch.uint8,
                      device=dev)
     out = torch.empty((B, w.heads_q, 128), dtype=torch.float32, device=dev)
     return dict(cache=cache, t_k=t_k, t_inv=t_inv, bt=bt, seq=seq, q=q, knew=knew, vnew=vnew,

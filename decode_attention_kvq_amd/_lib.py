@@ -16,6 +16,7 @@ NOALLOC_SCRATCH_BYTES = 32 << 20
 STATUS_NAMES = {0: "KVQ_OK", -1: "KVQ_ERR_INVALID_ARG", -2: "KVQ_ERR_UNSUPPORTED",
                 -3: "KVQ_ERR_WORKSPACE", -4: "KVQ_ERR_HIP"}
 EXPORTS = ("kvq_block_bytes", "kvq_quantize_append", "kvq_decode_workspace_bytes",
+           "kvq_decode_step_workspace_bytes",
            "kvq_decode_attn", "kvq_decode_attn_noalloc", "kvq_decode_step", "kvq_dequant", "kvq_window_bytes", "kvq_window_prefill",
            "kvq_window_workspace_bytes", "kvq_window_decode_attn", "kvq_window_decode_step",
            "kvq_status_string", "kvq_last_error")
@@ -58,6 +59,8 @@ def load():
     L.kvq_quantize_append.argtypes = [D, P, P, i32, i64, P, P, i32, P]
     L.kvq_decode_workspace_bytes.restype = sz
     L.kvq_decode_workspace_bytes.argtypes = [D, i32, i32, i32]
+    L.kvq_decode_step_workspace_bytes.restype = sz
+    L.kvq_decode_step_workspace_bytes.argtypes = [D, i32, i32, i32]
     L.kvq_decode_attn.restype = i32
     L.kvq_decode_attn.argtypes = [D, P, i32, i32, i32, P, P, i32, P, i32, f32, P, P, sz, P]
     L.kvq_decode_attn_noalloc.restype = i32

@@ -106,6 +106,13 @@ def decode_workspace_bytes(cache: KVCache, batch: int, num_q_heads: int, max_seq
     return int(load().kvq_decode_workspace_bytes(C.byref(d), batch, num_q_heads, max_seq_len))
 
 
+def decode_step_workspace_bytes(cache: KVCache, batch: int, num_q_heads: int, max_seq_len: int) -> int:
+    """Workspace bytes with which kvq_decode_step builds the decode's query operands beside
+    its append (batches of up to 512 sequences); decode_workspace_bytes is the minimum."""
+    d = cache.desc()
+    return int(load().kvq_decode_step_workspace_bytes(C.byref(d), batch, num_q_heads, max_seq_len))
+
+
 def _read_shapes(cache, q, block_table, seq_lens, t_k_inv_t, out, win_rows=None):
     """Shape checks shared by the read calls; returns (B, Hq)."""
     H = cache.num_kv_heads
@@ -184,7 +191,7 @@ def kvq_decode_step(cache: KVCache, q: torch.Tensor, k_new: torch.Tensor, v_new:
     _dev(out, "out", torch.float32)
     if sm_scale is None:
         sm_scale = 1.0 / math.sqrt(HEAD_DIM)
-    need = decode_workspace_bytes(cache, B, Hq, max_seq_len)
+    need = decode_step_workspace_bytes(cache, B, Hq, max_seq_len)
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()

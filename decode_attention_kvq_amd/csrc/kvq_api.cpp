@@ -100,6 +100,13 @@ int split_length(int max_seq_len, const kvq::WindowShape* win) {
   return win ? (max_seq_len > win->sink ? max_seq_len - win->sink : 0) : max_seq_len;
 }
 
+// Byte offset of a decode step's query-operand image in its workspace: after the decode's
+// partial outputs, 256-byte aligned.
+size_t step_qop_offset(const kvq_cache_desc* cache, int32_t batch, int32_t num_q_heads, int32_t max_seq_len) {
+  const kvq::DecodeSplit sp = kvq::decode_split(batch, cache->num_kv_heads, max_seq_len);
+  return (workspace_layout(batch, num_q_heads, sp.chunks).total + 255) & ~(size_t)255;
+}
+
 // Checks and fills the decode launch; shared by the plain and windowed decodes.  With
 // windows (win non-null) the partial results always go to the workspace.
 kvq_status decode_params(const kvq_cache_desc* cache, const void* q, kvq_dtype q_dtype, int32_t batch,
@@ -212,6 +219,18 @@ size_t kvq_decode_workspace_bytes(const kvq_cache_desc* cache, int32_t batch, in
   return workspace_layout(batch, num_q_heads, sp.chunks).total;
 }
 
+size_t kvq_decode_step_workspace_bytes(const kvq_cache_desc* cache, int32_t batch, int32_t num_q_heads,
+                                       int32_t max_seq_len) {
+  if (!cache || cache->num_kv_heads < 1 || batch <= 0 || num_q_heads < 1 || max_seq_len < 0 ||
+      num_q_heads % cache->num_kv_heads != 0 || num_q_heads / cache->num_kv_heads > 16)
+    return 0;
+  const kvq::DecodeSplit sp = kvq::decode_split(batch, cache->num_kv_heads, max_seq_len);
+  if (sp.chunks == 1 || batch > kvq::kStepPrepMaxTokens)   // no image: the decode's own workspace
+    return kvq_decode_workspace_bytes(cache, batch, num_q_heads, max_seq_len);
+  return step_qop_offset(cache, batch, num_q_heads, max_seq_len) +
+         (size_t)batch * cache->num_kv_heads * kvq::qop_dwords(kvq::decode_group_pad(num_q_heads / cache->num_kv_heads)) * 4;
+}
+
 kvq_status kvq_decode_attn(const kvq_cache_desc* cache, const void* q, kvq_dtype q_dtype, int32_t batch,
                            int32_t num_q_heads, const float* t_k_inv_t, const int32_t* block_table,
                            int32_t max_pages, const int32_t* seq_lens, int32_t max_seq_len, float sm_scale,
@@ -277,8 +296,25 @@ kvq_status kvq_decode_step(const kvq_cache_desc* cache, const void* q, const voi
   // two launches in stream order: the append, then the decode that reads it.  (Writing the
   // new token inside the decode kernel, by the workgroup that reads the last page, measured
   // slower: its latency lands at the start of every workgroup, before the page stream.)
+  // The query operands need no cache, so when the decode splits sequences over several
+  // workgroups (each of which would build the same operands) and the workspace has room
+  // for them, the append launch builds them once.  Without a split the decode builds them
+  // while its first pages load, which measured no slower than reading them.
   const kvq::AppendParams a = append_params(cache, k_new, v_new, new_slots, batch, t_k);
   const hipStream_t st = static_cast<hipStream_t>(stream);
+  if (p.chunks > 1 && batch <= kvq::kStepPrepMaxTokens &&
+      workspace_bytes >= kvq_decode_step_workspace_bytes(cache, batch, num_q_heads, max_seq_len)) {
+    // the append launch also builds the query operands, which the decode then reads
+    kvq::StepPrepParams sp;
+    sp.a = a;
+    sp.d = p;
+    sp.qop = reinterpret_cast<uint32_t*>(static_cast<char*>(workspace) +
+                                         step_qop_offset(cache, batch, num_q_heads, max_seq_len));
+    sp.n_tokens = batch;
+    if ((s = hip_status(kvq::launch_step_prep(sp, (int)dtype, cache->bits_k, st))) != KVQ_OK) return s;
+    p.qop = sp.qop;
+    return hip_status(kvq::launch_decode(p, cache->bits_k, cache->bits_v, (int)dtype, st));
+  }
   if ((s = hip_status(kvq::launch_append(a, (int)dtype, st))) != KVQ_OK) return s;
   return hip_status(kvq::launch_decode(p, cache->bits_k, cache->bits_v, (int)dtype, st));
 }

@@ -609,7 +609,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void a
 // Small batches (a decode step's new tokens): one workgroup per (token, KV head), so the
 // whole step is a few hundred instructions deep.  Lane l holds channels 2l and 2l+1.
 // ---------------------------------------------------------------------------------
-constexpr int kSmallMaxTokens = 512;    // at most this many tokens use the small path
+constexpr int kSmallMaxTokens = kSmallAppendMaxTokens;
 
 // Five waves per (token, KV head): waves 0-3 share the key transform, wave 0 then writes
 // the key and wave 4 the value.

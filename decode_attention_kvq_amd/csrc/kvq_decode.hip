@@ -44,6 +44,7 @@
 #include <type_traits>
 
 #include "kvq_device.h"
+#include "kvq_encode.h"
 #include "kvq_internal.h"
 
 namespace kvq {
@@ -267,6 +268,161 @@ struct IdentityMatrix {
 };
 __device__ constexpr IdentityMatrix kIdentity{};
 
+// ---- the query operands: q' = q T^-T (fp32, log2 units) as fp6 terms ----
+// One lane's share of them: the fp6 codes of the kQTerms terms for channels key_channel(kg, .)
+// of head gq = n % GP (kg = lane / 16), the head's scale exponent e1 and its sums of q' as
+// kQBase and kQTerms terms carry them (divided by F = 2: the product with the fp4 codes, of
+// value code / 2, gives half of q'.code).
+struct QOperands {
+  v8i bq6[kQTerms];
+  int e1;
+  float qsf3, qsf4;
+};
+constexpr float kF = 2.0f;                 // score = F * x'
+
+// The loads the build needs, issued first so that the page loads queue behind them: this
+// thread's q elements and, for lane (quad, cgrp) of wave w, columns j0 .. j0 + 3 (j0 = 32 w
+// + 4 quad) of rows 16 cgrp .. 16 cgrp + 15 of T^-T.
+template <typename TQ, int GP>
+struct QLoads {
+  static constexpr int QPER = (GP * kHeadDim + kThreads - 1) / kThreads;  // q elements per thread
+  float qreg[QPER];
+  f32x4 trow[16];
+};
+template <typename TQ, int GP>
+__device__ __forceinline__ void q_issue_loads(const DecodeParams& p, int b, int kvh, int wave, int lane,
+                                              QLoads<TQ, GP>& L) {
+  const int G = p.group;
+  const TQ* qb = reinterpret_cast<const TQ*>(p.q) + ((int64_t)b * p.heads_q + (int64_t)kvh * G) * kHeadDim;
+#pragma unroll
+  for (int k = 0; k < QLoads<TQ, GP>::QPER; ++k) {   // rows past the group read row 0 and are zeroed later
+    const int idx = (int)threadIdx.x + kThreads * k;
+    L.qreg[k] = Elem<TQ>::get(qb, idx < G * kHeadDim ? idx : idx % kHeadDim);
+  }
+  const int quad = lane & 7, cgrp = lane >> 3;
+  const int j0 = 32 * wave + 4 * quad;
+  // both candidates live in global memory; saying so keeps these global (not flat) loads,
+  // whose completion the compiler counts precisely
+  typedef __attribute__((address_space(1))) const f32x4 gf32x4;
+  const gf32x4* tsrc = (const gf32x4*)(p.tinv ? p.tinv + (int64_t)kvh * kHeadDim * kHeadDim : kIdentity.v);
+#pragma unroll
+  for (int cc = 0; cc < 16; ++cc) L.trow[cc] = tsrc[((16 * cgrp + cc) * kHeadDim + j0) / 4];
+}
+
+// Builds this lane's operands from the loads (every thread of the 4-wave workgroup calls it:
+// it holds three workgroup barriers).  qs: LDS scratch of GP * kQRow floats, q first (rows
+// of kHeadDim), then q' (rows of kQRow: each 32-channel group in 33 floats, so that the 16
+// (head, group) operands read at once hit distinct banks).
+constexpr int kQRow = 4 * 33;
+template <typename TQ, int BK, int GP>
+__device__ __forceinline__ void q_build(const DecodeParams& p, int wave, int lane, const QLoads<TQ, GP>& L,
+                                        float* qs, QOperands& o) {
+  const int G = p.group;
+  const int kg = lane >> 4, n = lane & 15;
+  const int quad = lane & 7, cgrp = lane >> 3;
+#pragma unroll
+  for (int k = 0; k < QLoads<TQ, GP>::QPER; ++k) {
+    const int idx = (int)threadIdx.x + kThreads * k;
+    if (idx < GP * kHeadDim) qs[idx] = idx < G * kHeadDim ? L.qreg[k] : 0.0f;
+  }
+  lds_barrier();
+  float qacc[GP][4];
+#pragma unroll
+  for (int g = 0; g < GP; ++g) {
+    float a4[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int cc = 0; cc < 16; cc += 4) {
+      const float4 qv = *reinterpret_cast<const float4*>(qs + g * kHeadDim + 16 * cgrp + cc);
+      const float qq[4] = {qv.x, qv.y, qv.z, qv.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) a4[k] = __builtin_fmaf(qq[e], L.trow[cc + e][k], a4[k]);
+      }
+    }
+    // sum over the 8 row groups (lane bits 3..5): xor 8 by a row rotation, then the swaps
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int u = __builtin_bit_cast(int, a4[k]);
+      const float v = a4[k] + __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(u, 0x128, 0xF, 0xF, false));
+      qacc[g][k] = col_sum(v);
+    }
+  }
+  lds_barrier();                           // every read of q is done: q' replaces it
+  if (cgrp == 0) {
+    // channels j0 .. j0 + 3 sit in group j0 / 32 = wave; heads past G read as 0
+#pragma unroll
+    for (int g = 0; g < GP; ++g)
+#pragma unroll
+      for (int k = 0; k < 4; ++k) qs[g * kQRow + 33 * wave + 4 * quad + k] = g < G ? qacc[g][k] * p.score_scale : 0.0f;
+  }
+  lds_barrier();
+  // q' as fp6 (e2m3) terms t_k with scales 2^(e1 - 4k), e1 per head so that
+  // max|q'| 2^-e1 <= 7.5; each term holds the previous remainder to within a quarter of its
+  // scale.  Every lane builds its own operand, the channels key_channel(kg, j) of head gq,
+  // with the fp6 packing conversion, and converts it back for the remainder.
+  const int gq = n % GP;
+  // a[i], b[i]: channels key_channel(kg, 2i), key_channel(kg, 2i + 1) (the packing puts
+  // a[i] at element 2i and b[i] at 2i + 1), then the remainders
+  f32x16 a, b;
+  const float* qh = qs + gq * kQRow + 33 * kg;
+  float amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    a[i] = qh[key_channel<BK>(0, 2 * i)];
+    b[i] = qh[key_channel<BK>(0, 2 * i + 1)];
+    amax = fmaxf(amax, fmaxf(fabsf(a[i]), fabsf(b[i])));
+  }
+  amax = col_max(amax);                  // over the four lane groups: the whole head
+  int e1 = 0;
+  if (amax > 0.0f) {
+    const int E = ilogbf(amax);
+    e1 = ldexpf(amax, 2 - E) <= 7.5f ? E - 2 : E - 1;
+  }
+  e1 = max(e1, -126 + 4 * (kQTerms - 1));   // the last term's scale stays a normal E8M0 value
+  float s3 = 0.0f, s4 = 0.0f;
+#pragma unroll
+  for (int k = 0; k < kQTerms; ++k) {
+    const float scale = ldexpf(1.0f, e1 - 4 * k);
+    const u32x6 code = fp6_pack32(a, b, scale);
+    const half32 h = fp6_unpack32_f16(code);          // the term's values / scale (exact)
+    if (k + 1 < kQTerms) {                            // (the last remainder is not used)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        a[i] = __builtin_fmaf(-(float)h[2 * i], scale, a[i]);
+        b[i] = __builtin_fmaf(-(float)h[2 * i + 1], scale, b[i]);
+      }
+    }
+    // the term's sum by a packed fp16 tree: its values are multiples of 1/8 of magnitude at
+    // most 7.5, so every partial sum is a multiple of 1/8 below 256 in magnitude, where fp16
+    // is exact (steps of 1/8 from 128 to 256)
+    half2_t hp[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) hp[i] = half2_t{h[2 * i], h[2 * i + 1]};
+#pragma unroll
+    for (int w = 8; w >= 1; w >>= 1)
+#pragma unroll
+      for (int i = 0; i < w; ++i) hp[i] = hp[i] + hp[i + w];
+    const float hs = (float)hp[0][0] + (float)hp[0][1];
+    if (k < kQBase) s3 += hs * scale;
+    s4 += hs * scale;
+#pragma unroll
+    for (int d = 0; d < 6; ++d) o.bq6[k][d] = (int)code[d];
+    o.bq6[k][6] = 0;
+    o.bq6[k][7] = 0;
+  }
+  o.e1 = e1;
+  o.qsf3 = gq < G ? col_sum(s3) / kF : 0.0f;
+  o.qsf4 = gq < G ? col_sum(s4) / kF : 0.0f;
+}
+
+// The operands of (sequence b, KV head kvh) in a step's image: for each head gq < GP and
+// channel group kg the 6 x kQTerms code words (at 24 (4 gq + kg)), then per head (e1, qsf3,
+// qsf4, 0) at 96 GP + 4 gq.  Written by the lanes of wave 0 with n < GP (one per (gq, kg)).
+__device__ __forceinline__ const uint32_t* qop_base(const uint32_t* img, int b, int kvh, int heads_kv, int gp) {
+  return img + ((int64_t)b * heads_kv + kvh) * qop_dwords(gp);
+}
+
 template <typename TQ, int BK, int BV, int GP>
 __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
   constexpr int NB = 16 / GP;        // column blocks
@@ -283,10 +439,6 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
   // merge buffers (per wave: 16 columns x 128 channels in rows of kHeadDim + 1, so that the
   // scattered writes of a half wave reach 32 banks; then 16 x (m, l))
   __shared__ __attribute__((aligned(16))) uint8_t smem[kWaves * 16 * (kHeadDim + 3) * 4];
-  // prologue scratch: q (rows of kHeadDim), then q' (rows of kQRow: each 32-channel group in
-  // 33 floats, so that the 16 (head, group) operands read at once hit distinct banks)
-  constexpr int kQRow = 4 * 33;
-  __shared__ __attribute__((aligned(16))) float qs[GP * kQRow];
 
   // ---- this wave's pages ----
   // with full-precision windows the cache holds the quantized middle positions only
@@ -326,140 +478,59 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
                          block_rsrc(p.vpool + blk * VB, pid >= 0 ? VB : 0), lo);
   };
 
-  // ---- prologue: q' = q T^-T (fp32, log2 units), then the fp16 operand ----
-  // Loads of q and T^-T go out first, then the first pages' loads, so the arithmetic below
-  // overlaps the page fetch.
-  constexpr int QPER = (GP * kHeadDim + kThreads - 1) / kThreads;  // q elements per thread
-  const TQ* qb = reinterpret_cast<const TQ*>(p.q) + ((int64_t)b * p.heads_q + (int64_t)kvh * G) * kHeadDim;
-  float qreg[QPER];
-#pragma unroll
-  for (int k = 0; k < QPER; ++k) {   // rows past the group read row 0 and are zeroed below
-    const int idx = (int)threadIdx.x + kThreads * k;
-    qreg[k] = Elem<TQ>::get(qb, idx < G * kHeadDim ? idx : idx % kHeadDim);
-  }
-  // lane (quad, cgrp) of wave w < 4: columns j0..j0+3 (j0 = 32w + 4 quad) of rows
-  // 16 cgrp..+15; the other waves take no part in the product
-  const bool tw = wave < 4;
-  const int quad = lane & 7, cgrp = lane >> 3;
-  const int j0 = 32 * (tw ? wave : 0) + 4 * quad;
-  // both candidates live in global memory; saying so keeps these global (not flat) loads,
-  // whose completion the compiler counts precisely
-  typedef __attribute__((address_space(1))) const f32x4 gf32x4;
-  const gf32x4* tsrc = (const gf32x4*)(p.tinv ? p.tinv + (int64_t)kvh * kHeadDim * kHeadDim : kIdentity.v);
-  f32x4 trow[16];
-#pragma unroll
-  for (int cc = 0; cc < 16; ++cc) trow[cc] = tw ? tsrc[((16 * cgrp + cc) * kHeadDim + j0) / 4] : f32x4{};
+  // ---- prologue: the query operands ----
+  // Computed here (q and T^-T loads first, then the first pages' loads, so the arithmetic
+  // overlaps the page fetch), or, in a decode step, read from the image that the step's
+  // append launch built.
+  const bool pre = p.qop != nullptr;
+  QLoads<TQ, GP> L;
+  if (!pre) q_issue_loads<TQ, GP>(p, b, kvh, wave, lane, L);
   my_page = (lane < np && my_page >= 0 && my_page < p.num_pages) ? my_page : -1;
   PageRegs<BK, BV, A> ring[PIPE];
 #pragma unroll
   for (int d = 0; d < PIPE; ++d) load(ring[d], d);
+  __shared__ __attribute__((aligned(16))) float qs[GP * kQRow];
+  QOperands qo;
+  if (pre) {
+    // the image's words of this lane's (head, channel group), then the head's scale
+    // exponent and sums (loaded and used in this one block)
+    const int gq = n % GP;
+    const uint32_t* base = qop_base(p.qop, b, kvh, p.heads_kv, GP);
+    const u32x4* src = reinterpret_cast<const u32x4*>(base + 24 * (4 * gq + kg));
+    u32x4 qw[7];
 #pragma unroll
-  for (int k = 0; k < QPER; ++k) {
-    const int idx = (int)threadIdx.x + kThreads * k;
-    if (idx < GP * kHeadDim) qs[idx] = idx < G * kHeadDim ? qreg[k] : 0.0f;
-  }
-  lds_barrier();
-  float qacc[GP][4];
-#pragma unroll
-  for (int g = 0; g < GP; ++g) {
-    float a4[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-    for (int cc = 0; cc < 16; cc += 4) {
-      const float4 qv = *reinterpret_cast<const float4*>(qs + g * kHeadDim + 16 * cgrp + cc);
-      const float qq[4] = {qv.x, qv.y, qv.z, qv.w};
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-#pragma unroll
-        for (int k = 0; k < 4; ++k) a4[k] = __builtin_fmaf(qq[e], trow[cc + e][k], a4[k]);
-      }
-    }
-    // sum over the 8 row groups (lane bits 3..5): xor 8 by a row rotation, then the swaps
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const int u = __builtin_bit_cast(int, a4[k]);
-      const float v = a4[k] + __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(u, 0x128, 0xF, 0xF, false));
-      qacc[g][k] = col_sum(v);
-    }
-  }
-  lds_barrier();                           // every read of q is done: q' replaces it
-  if (tw && cgrp == 0) {
-    // channels j0 .. j0 + 3 sit in group j0 / 32 = wave; heads past G read as 0
-#pragma unroll
-    for (int g = 0; g < GP; ++g)
-#pragma unroll
-      for (int k = 0; k < 4; ++k) qs[g * kQRow + 33 * wave + 4 * quad + k] = g < G ? qacc[g][k] * p.score_scale : 0.0f;
-  }
-  lds_barrier();
-  // q' as fp6 (e2m3) terms t_k with scales 2^(e1 - 4k), e1 per head so that
-  // max|q'| 2^-e1 <= 7.5; each term holds the previous remainder to within a quarter of its
-  // scale.  Every lane builds its own operand, the channels key_channel(kg, j) of head gq,
-  // with the fp6 packing conversion, and converts it back for the remainder.  The product
-  // with the fp4 codes (value c/2) gives half of q'.code: F = 2.
-  v8i bq6[kQTerms];
-  int sreg[kQTerms];
-  const int gq = n % GP;
-  constexpr float F = 2.0f;                                              // score = F * x'
-  float qsf3, qsf4;                      // sum(q') as carried by kQBase and kQTerms terms, / F
-  {
-    // a[i], b[i]: channels key_channel(kg, 2i), key_channel(kg, 2i + 1) (the packing puts
-    // a[i] at element 2i and b[i] at 2i + 1), then the remainders
-    f32x16 a, b;
-    const float* qh = qs + gq * kQRow + 33 * kg;
-    float amax = 0.0f;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      a[i] = qh[key_channel<BK>(0, 2 * i)];
-      b[i] = qh[key_channel<BK>(0, 2 * i + 1)];
-      amax = fmaxf(amax, fmaxf(fabsf(a[i]), fabsf(b[i])));
-    }
-    amax = col_max(amax);                  // over the four lane groups: the whole head
-    int e1 = 0;
-    if (amax > 0.0f) {
-      const int E = ilogbf(amax);
-      e1 = ldexpf(amax, 2 - E) <= 7.5f ? E - 2 : E - 1;
-    }
-    e1 = max(e1, -126 + 4 * (kQTerms - 1));   // the last term's scale stays a normal E8M0 value
-    float s3 = 0.0f, s4 = 0.0f;
+    for (int i = 0; i < 6; ++i) qw[i] = src[i];
+    qw[6] = *reinterpret_cast<const u32x4*>(base + 96 * GP + 4 * gq);
 #pragma unroll
     for (int k = 0; k < kQTerms; ++k) {
-      const float scale = ldexpf(1.0f, e1 - 4 * k);
-      const u32x6 code = fp6_pack32(a, b, scale);
-      const half32 h = fp6_unpack32_f16(code);          // the term's values / scale (exact)
-      if (k + 1 < kQTerms) {                            // (the last remainder is not used)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          a[i] = __builtin_fmaf(-(float)h[2 * i], scale, a[i]);
-          b[i] = __builtin_fmaf(-(float)h[2 * i + 1], scale, b[i]);
-        }
-      }
-      // the term's sum by a packed fp16 tree: its values are multiples of 1/8 of magnitude at
-      // most 7.5, so every partial sum is a multiple of 1/8 below 256 in magnitude, where fp16
-      // is exact (steps of 1/8 from 128 to 256)
-      half2_t hp[16];
-#pragma unroll
-      for (int i = 0; i < 16; ++i) hp[i] = half2_t{h[2 * i], h[2 * i + 1]};
-#pragma unroll
-      for (int w = 8; w >= 1; w >>= 1)
-#pragma unroll
-        for (int i = 0; i < w; ++i) hp[i] = hp[i] + hp[i + w];
-      const float hs = (float)hp[0][0] + (float)hp[0][1];
-      if (k < kQBase) s3 += hs * scale;
-      s4 += hs * scale;
-#pragma unroll
-      for (int d = 0; d < 6; ++d) bq6[k][d] = (int)code[d];
-      bq6[k][6] = 0;
-      bq6[k][7] = 0;
-      // scale byte t (selected per tile by op_sel): the term's scale for this lane's column
-      // block, 2^-127 (contributes nothing) for the others
-      uint32_t sc = 0;
-#pragma unroll
-      for (int t = 0; t < NB; ++t) sc |= (beta == t ? (uint32_t)(127 + e1 - 4 * k) : 0u) << (8 * t);
-      sreg[k] = (int)sc;
+      for (int d = 0; d < 6; ++d) qo.bq6[k][d] = (int)qw[(6 * k + d) / 4][(6 * k + d) % 4];
+      qo.bq6[k][6] = 0;
+      qo.bq6[k][7] = 0;
     }
-    qsf3 = gq < G ? col_sum(s3) / F : 0.0f;
-    qsf4 = gq < G ? col_sum(s4) / F : 0.0f;
+    // each vector element goes through a scalar first: __builtin_bit_cast of an element of
+    // an ext_vector_type lvalue reads element 0
+    const uint32_t w0 = qw[6][0], w1 = qw[6][1], w2 = qw[6][2];
+    qo.e1 = (int)w0;
+    qo.qsf3 = __builtin_bit_cast(float, w1);
+    qo.qsf4 = __builtin_bit_cast(float, w2);
+  } else {
+    q_build<TQ, BK, GP>(p, wave, lane, L, qs, qo);
   }
-
+  v8i bq6[kQTerms];
+  int sreg[kQTerms];
+  constexpr float F = kF;
+  const float qsf3 = qo.qsf3, qsf4 = qo.qsf4;
+#pragma unroll
+  for (int k = 0; k < kQTerms; ++k) {
+    bq6[k] = qo.bq6[k];
+    // scale byte t (selected per tile by op_sel): the term's scale for this lane's column
+    // block, 2^-127 (contributes nothing) for the others
+    uint32_t sc = 0;
+#pragma unroll
+    for (int t = 0; t < NB; ++t) sc |= (beta == t ? (uint32_t)(127 + qo.e1 - 4 * k) : 0u) << (8 * t);
+    sreg[k] = (int)sc;
+  }
 
   // per (accumulator a, row r): token u = 4*(a*NB + beta) + r of this lane group
   f32x4 acc_o[8];
@@ -910,6 +981,61 @@ hipError_t launch_bits(const DecodeParams& p, int q_dtype, hipStream_t stream) {
   }
 }
 
+// A decode step's first launch.  Workgroups x < n_tokens append token x for KV head y (the
+// small append path's work, with 4 waves: wave 1 writes the value); the others build the
+// query operands of (sequence x - n_tokens, KV head y) with the decode kernel's own code and
+// store them in the image.  The operands do not depend on the cache, so they are built while
+// the append runs instead of at the start of every decode workgroup.
+template <typename TIn, int KSEL, int BK, int GP>
+__global__ __launch_bounds__(kThreads) void step_prep_kernel(StepPrepParams sp) {
+  constexpr int kLdsFloats = GP * kQRow > 4 * kHeadDim ? GP * kQRow : 4 * kHeadDim;
+  __shared__ __attribute__((aligned(16))) float lds[kLdsFloats];
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  if ((int)blockIdx.x < sp.n_tokens) {
+    append_token<TIn, KSEL, 1>(sp.a, blockIdx.x, blockIdx.y, wave, lane, reinterpret_cast<float (*)[kHeadDim]>(lds));
+    return;
+  }
+  const int b = (int)blockIdx.x - sp.n_tokens, kvh = blockIdx.y;
+  QLoads<TIn, GP> L;
+  q_issue_loads<TIn, GP>(sp.d, b, kvh, wave, lane, L);
+  QOperands o;
+  q_build<TIn, BK, GP>(sp.d, wave, lane, L, lds, o);
+  const int kg = lane >> 4, n = lane & 15;
+  if (wave == 0 && n < GP) {
+    uint32_t* base = sp.qop + ((int64_t)b * sp.d.heads_kv + kvh) * qop_dwords(GP);
+    u32x4* dst = reinterpret_cast<u32x4*>(base + 24 * (4 * n + kg));
+#pragma unroll
+    for (int i = 0; i < 6; ++i) {
+      u32x4 w;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) w[j] = (uint32_t)o.bq6[(4 * i + j) / 6][(4 * i + j) % 6];
+      dst[i] = w;
+    }
+    if (kg == 0)
+      *reinterpret_cast<u32x4*>(base + 96 * GP + 4 * n) =
+          u32x4{(uint32_t)o.e1, __builtin_bit_cast(uint32_t, o.qsf3), __builtin_bit_cast(uint32_t, o.qsf4), 0u};
+  }
+}
+
+template <typename TIn, int KSEL, int BK>
+hipError_t launch_prep_gp(const StepPrepParams& sp, hipStream_t stream) {
+  const dim3 grid((unsigned)(sp.n_tokens + sp.d.batch), (unsigned)sp.d.heads_kv);
+  switch (sp.d.gpad) {
+    case 4: hipLaunchKernelGGL((step_prep_kernel<TIn, KSEL, BK, 4>), grid, dim3(kThreads), 0, stream, sp); break;
+    case 8: hipLaunchKernelGGL((step_prep_kernel<TIn, KSEL, BK, 8>), grid, dim3(kThreads), 0, stream, sp); break;
+    default: hipLaunchKernelGGL((step_prep_kernel<TIn, KSEL, BK, 16>), grid, dim3(kThreads), 0, stream, sp); break;
+  }
+  return hipGetLastError();
+}
+
+template <typename TIn>
+hipError_t launch_prep_typed(const StepPrepParams& sp, int bits_k, hipStream_t stream) {
+  // the small path's percentile networks; key channel order of 4-bit keys or of the others
+  const bool k3 = select_width(sp.a) == 3;
+  if (bits_k == 4) return k3 ? launch_prep_gp<TIn, 3, 4>(sp, stream) : launch_prep_gp<TIn, 0, 4>(sp, stream);
+  return k3 ? launch_prep_gp<TIn, 3, 2>(sp, stream) : launch_prep_gp<TIn, 0, 2>(sp, stream);
+}
+
 }  // namespace
 
 int decode_group_pad(int group) { return group <= 4 ? 4 : (group <= 8 ? 8 : 16); }
@@ -968,6 +1094,14 @@ hipError_t launch_decode(const DecodeParams& p, int bits_k, int bits_v, int q_dt
     case 42: return launch_bits<4, 2>(p, q_dtype, stream);
     case 43: return launch_bits<4, 3>(p, q_dtype, stream);
     default: return launch_bits<4, 4>(p, q_dtype, stream);
+  }
+}
+
+hipError_t launch_step_prep(const StepPrepParams& sp, int dtype, int bits_k, hipStream_t stream) {
+  switch (dtype) {
+    case 0: return launch_prep_typed<float>(sp, bits_k, stream);
+    case 1: return launch_prep_typed<__bf16>(sp, bits_k, stream);
+    default: return launch_prep_typed<_Float16>(sp, bits_k, stream);
   }
 }
 

@@ -126,6 +126,15 @@ kvq_status kvq_quantize_append(const kvq_cache_desc* cache, const void* k, const
 size_t kvq_decode_workspace_bytes(const kvq_cache_desc* cache, int32_t batch,
                                   int32_t num_q_heads, int32_t max_seq_len);
 
+/* Workspace bytes with which kvq_decode_step builds the query operands beside its append.
+ * When the decode splits each sequence over several workgroups and batch <= 512:
+ * kvq_decode_workspace_bytes() plus an image of 400 bytes per query head, rounded up to
+ * 4, 8 or 16 per KV head, for every (sequence, KV head), with the same partial-output
+ * region as kvq_decode_attn first.  Otherwise the step builds no image and this equals
+ * kvq_decode_workspace_bytes().  0 for invalid arguments. */
+size_t kvq_decode_step_workspace_bytes(const kvq_cache_desc* cache, int32_t batch,
+                                       int32_t num_q_heads, int32_t max_seq_len);
+
 /* Read path: one decode step of grouped-query attention over the quantized cache.
  *   q            device, [batch][num_q_heads][128] of q_dtype (post-RoPE queries);
  *                num_q_heads must be a multiple of num_kv_heads, at most 16 query
@@ -182,8 +191,15 @@ kvq_status kvq_decode_attn_noalloc(const kvq_cache_desc* cache, const void* q, k
  *                 < 0 or >= num_pages*64: no new token for that sequence.  Another slot
  *                 is written, but the output may then miss it.
  *   t_k           as in kvq_quantize_append (t_dtype must equal dtype); t_k_inv_t,
- *                 block_table, seq_lens, max_seq_len, sm_scale, out, workspace as in
- *                 kvq_decode_attn (the workspace size is kvq_decode_workspace_bytes()).
+ *                 block_table, seq_lens, max_seq_len, sm_scale, out as in kvq_decode_attn.
+ *   workspace     device scratch, owned by the caller, of at least
+ *                 kvq_decode_workspace_bytes() bytes (KVQ_ERR_WORKSPACE otherwise).  With
+ *                 kvq_decode_step_workspace_bytes() bytes, when the decode splits each
+ *                 sequence over several workgroups and batch <= 512, the first launch also
+ *                 builds the decode's query operands (q' = q . T_K^-T as fp6 terms) for
+ *                 every (sequence, KV head) while it appends, and the decode reads them
+ *                 instead of building them in every workgroup; the output is the same bit
+ *                 for bit.
  * The written bytes equal those of kvq_quantize_append for the same new tokens. */
 kvq_status kvq_decode_step(const kvq_cache_desc* cache, const void* q, const void* k_new,
                            const void* v_new, kvq_dtype dtype, int32_t batch,

@@ -58,7 +58,7 @@ def _setup(rng, B, H, G, lens, bits, quant, dtype, transform, config=1):
     return dict(P=P, bt=bt, kp=kp, vp=vp, t=t, tinv=tinv, kw=kw, knew=knew, vnew=vnew, new_slots=new_slots, q=q)
 
 
-def _gpu(s, H, bits, quant, dtype, lens, fused=True):
+def _gpu(s, H, bits, quant, dtype, lens, fused=True, min_workspace=False):
     tdt = {"bf16": torch.bfloat16, "f16": torch.float16, "f32": torch.float32}[dtype]
     cache = api.KVCache(s["P"], H, bits[0], bits[1], quant[0], quant[1],
                         k_pages=torch.from_numpy(s["kp"].copy()).cuda(),
@@ -71,7 +71,13 @@ def _gpu(s, H, bits, quant, dtype, lens, fused=True):
     seq = torch.tensor(lens, dtype=torch.int32).cuda()
     t = None if s["t"] is None else torch.from_numpy(s["t"]).to(tdt).cuda()
     tinv = None if s["tinv"] is None else torch.from_numpy(s["tinv"]).cuda()
-    if fused:
+    if fused and min_workspace:
+        # only the decode's partial outputs: the decode builds the query operands itself
+        need = api.decode_workspace_bytes(cache, len(lens), q.shape[1], max(lens))
+        ws = torch.empty(max(need, 1), dtype=torch.uint8, device="cuda")
+        assert need < api.decode_step_workspace_bytes(cache, len(lens), q.shape[1], max(lens))
+        out = api.kvq_decode_step(cache, q, kn, vn, sl, bt, seq, max(lens), t_k=t, t_k_inv_t=tinv, workspace=ws)
+    elif fused:
         out = api.kvq_decode_step(cache, q, kn, vn, sl, bt, seq, max(lens), t_k=t, t_k_inv_t=tinv)
     else:
         api.kvq_quantize_append(cache, kn, vn, sl, t_k=t)
@@ -114,3 +120,30 @@ def test_fused_step_matches_append_then_decode(case):
     assert np.array_equal(vf, vp), describe_mismatch(vf, vp)
     if not transform:
         assert np.array_equal(kf, kp), describe_mismatch(kf, kp)
+
+
+# Shapes the decode splits over several workgroups per sequence: the step then builds the
+# query operands in its append launch (cases 2 and 3 above, and these).
+IMAGE_CASES = [CASES[2], CASES[3],
+    (2, 2, 4, [5000, 1300], (3, 3), ("percentile", "percentile"), "bf16", True),
+    (1, 1, 16, [4200], (2, 4), ("rms", "percentile"), "f16", False),
+    (3, 2, 1, [2049, 64, 1], (4, 2), ("percentile", "rms"), "f32", True),
+    (1, 2, 8, [6000], (2, 3), ("percentile", "percentile"), "bf16", True),
+]
+
+
+@pytest.mark.parametrize("case", range(len(IMAGE_CASES)))
+def test_step_query_operands_built_beside_the_append(case):
+    """With the step's full workspace the append launch builds the decode's query operands
+    (q' = q T^-T as fp6 terms) and the decode reads them; with only the decode's workspace
+    the decode builds them itself.  Both run the same code: the outputs and the written
+    pages are identical bit for bit, and equal to the separate append + decode."""
+    B, H, G, lens, bits, quant, dtype, transform = IMAGE_CASES[case]
+    rng = np.random.default_rng(100 + case)
+    s = _setup(rng, B, H, G, lens, bits, quant, dtype, transform)
+    out_i, ki, vi = _gpu(s, H, bits, quant, dtype, lens, fused=True)
+    out_m, km, vm = _gpu(s, H, bits, quant, dtype, lens, fused=True, min_workspace=True)
+    out_s, _, _ = _gpu(s, H, bits, quant, dtype, lens, fused=False)
+    assert np.array_equal(ki, km) and np.array_equal(vi, vm)
+    assert np.array_equal(out_i, out_m), np.abs(out_i - out_m).max()
+    assert np.array_equal(out_i, out_s), np.abs(out_i - out_s).max()
