@@ -200,7 +200,8 @@ def test_qwen3_8b_b1_16k_full():
     flipped codes from fp32 vs fp64 transform accumulation, scale/zero off by one fp16 ulp
     on <= 2e-4 of groups), the GPU decode of the GPU-written pools with the oracle's decode
     of the same pools, and the GPU write + decode with the oracle write + decode, all rows
-    at 2e-3 row-relative."""
+    at 2e-3 row-relative.  Then the same for one decode step (kvq_decode_step) that rewrites
+    the last position, in the benchmark's configuration."""
     w = synth.WORKLOADS["qwen3-8b-b1-16k"]
     H, n = w.heads_kv, w.seq_len
     t, tinv = _transforms(w.config, H, w.group)
@@ -235,6 +236,30 @@ def test_qwen3_8b_b1_16k_full():
     got = out.cpu().numpy()
     ref_g = oracle.decode_attention(gk, cache.v_pages.cpu().numpy(), q, bt, seq, t_inv_t=tinv,
                                     bits_k=2, bits_v=2)
+    assert row_rel_err(got, ref_g).max() <= TOL
+    assert row_rel_err(got, ref).max() <= TOL
+    # a decode step as the benchmark runs it: the new token rewrites the last position, and
+    # with the step's full workspace the append launch also builds the query operands that
+    # the 16 chunks read
+    rng_new = np.random.default_rng(12)
+    kn = rng_new.standard_normal((1, H, 128)).astype(np.float32)
+    vn = rng_new.standard_normal((1, H, 128)).astype(np.float32)
+    kn = torch.from_numpy(kn).to(torch.bfloat16)
+    vn = torch.from_numpy(vn).to(torch.bfloat16)
+    new_slot = slots[n - 1:n].copy()
+    need = api.decode_step_workspace_bytes(cache, 1, w.heads_q, n)
+    assert need > api.decode_workspace_bytes(cache, 1, w.heads_q, n)
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+    out = api.kvq_decode_step(cache, torch.from_numpy(q).to(torch.bfloat16).cuda(), kn.cuda(), vn.cuda(),
+                              torch.from_numpy(new_slot).cuda(), torch.from_numpy(bt).cuda(),
+                              torch.from_numpy(seq).cuda(), n, t_k=torch.from_numpy(t).to(torch.bfloat16).cuda(),
+                              t_k_inv_t=torch.from_numpy(tinv).cuda(), workspace=ws)
+    got = out.cpu().numpy()
+    oracle.append(kp, vp, kn.float().numpy(), vn.float().numpy(), new_slot, t_k=t, bits_k=2, bits_v=2)
+    gv = cache.v_pages.cpu().numpy()
+    assert np.array_equal(gv, vp)
+    ref = oracle.decode_attention(kp, vp, q, bt, seq, t_inv_t=tinv, bits_k=2, bits_v=2)
+    ref_g = oracle.decode_attention(cache.k_pages.cpu().numpy(), gv, q, bt, seq, t_inv_t=tinv, bits_k=2, bits_v=2)
     assert row_rel_err(got, ref_g).max() <= TOL
     assert row_rel_err(got, ref).max() <= TOL
 

@@ -9,6 +9,12 @@ decode, and:
     (measured 4.6e-5 to 1.07e-4 per sequence);
   * the GPU output matches the oracle's decode of the GPU-written pages, and the oracle's
     write + decode, within 2e-3 per (sequence, query head) row.
+Then one decode step (kvq_decode_step) in the benchmark's configuration: a new token
+rewrites every sequence's last position, with the step's full workspace (the long-context
+workload splits its sequences, so the step's append launch also builds the decode's query
+operands).  The sampled sequences' value pages equal the oracle's append of the same token
+into its pages bit for bit, and the output is within 2e-3 of the oracle's decode of the
+GPU's pages and of its own pages.
 Write path: "WUSH-KV: KV Cache Quantization with Data-Adaptive Transforms" §4.2, §4.3
 (QuEST, alpha = 2.83, on the long-context workload) and §5.3 (percentile 1%/99%); read
 path: §4.1, §4.2; long contexts as in its App. D.3.
@@ -60,10 +66,13 @@ def test_full_size_end_to_end(name, samples):
             kept[b] = (k.float().cpu().numpy(), v.float().cpu().numpy())
     q = synth.decode_queries(w)
     seq = np.full(B, n, np.int32)
-    out = api.kvq_decode_attn(cache, torch.from_numpy(q).to(torch.bfloat16).to(dev), torch.from_numpy(bt).to(dev),
-                              torch.from_numpy(seq).to(dev), n, t_k_inv_t=torch.from_numpy(tinv).to(dev))
+    q_dev, bt_dev, seq_dev = (torch.from_numpy(q).to(torch.bfloat16).to(dev), torch.from_numpy(bt).to(dev),
+                              torch.from_numpy(seq).to(dev))
+    tinv_dev = torch.from_numpy(tinv).to(dev)
+    out = api.kvq_decode_attn(cache, q_dev, bt_dev, seq_dev, n, t_k_inv_t=tinv_dev)
     torch.cuda.synchronize()
     got = out.cpu().numpy()
+    oracle_pools = {}
     for b in picks:
         pages = bt[b]
         gk = cache.k_pages[torch.from_numpy(pages).long().to(dev)].cpu().numpy()
@@ -90,4 +99,34 @@ def test_full_size_end_to_end(name, samples):
         e_g = row_rel_err(got[b], ref_g).max()
         e = row_rel_err(got[b], ref).max()
         print(f"  sequence {b}: row-relative error vs oracle on GPU pages {e_g:.2e}, end to end {e:.2e}", flush=True)
+        assert e_g <= TOL and e <= TOL, (b, e_g, e)
+        oracle_pools[b] = (kp, vp)
+
+    # the step: each sequence's new token rewrites its last position
+    knew, vnew = synth.kv_tokens_torch(w, B, dev, seq=10_000)
+    new_slots = np.array([bt[b, (n - 1) // 64] * 64 + (n - 1) % 64 for b in range(B)], np.int64)
+    need = api.decode_step_workspace_bytes(cache, B, w.heads_q, n)
+    assert (need > api.decode_workspace_bytes(cache, B, w.heads_q, n)) == (name == "long-b16-128k-quest")
+    ws = torch.empty(max(1, need), dtype=torch.uint8, device=dev)
+    out = api.kvq_decode_step(cache, q_dev, knew, vnew, torch.from_numpy(new_slots).to(dev), bt_dev, seq_dev, n,
+                              t_k=t_dev, t_k_inv_t=tinv_dev, workspace=ws)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    kn, vn = knew.float().cpu().numpy(), vnew.float().cpu().numpy()
+    for b in picks:
+        pages = bt[b]
+        gk = cache.k_pages[torch.from_numpy(pages).long().to(dev)].cpu().numpy()
+        gv = cache.v_pages[torch.from_numpy(pages).long().to(dev)].cpu().numpy()
+        kp, vp = oracle_pools[b]
+        oracle.append(kp, vp, kn[b:b + 1], vn[b:b + 1], np.array([n - 1], np.int64), t_k=t, bits_k=w.bits_k,
+                      bits_v=w.bits_v, quant_k=qcode, quant_v=qcode, p_lo=w.p_lo, p_hi=w.p_hi, alpha_k=w.alpha,
+                      alpha_v=w.alpha)
+        assert np.array_equal(gv, vp), b
+        all_pages = np.arange(pps)
+        ref_g = oracle_decode_sequence(gk, gv, q[b], all_pages, n, t_inv_t=tinv, bits_k=w.bits_k, bits_v=w.bits_v)
+        ref = oracle_decode_sequence(kp, vp, q[b], all_pages, n, t_inv_t=tinv, bits_k=w.bits_k, bits_v=w.bits_v)
+        e_g = row_rel_err(got[b], ref_g).max()
+        e = row_rel_err(got[b], ref).max()
+        print(f"  step, sequence {b}: row-relative error vs oracle on GPU pages {e_g:.2e}, end to end {e:.2e}",
+              flush=True)
         assert e_g <= TOL and e <= TOL, (b, e_g, e)
