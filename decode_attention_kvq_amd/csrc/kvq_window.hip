@@ -129,27 +129,38 @@ __global__ __launch_bounds__(kWinThreads) void window_kernel(DecodeParams p, Win
     dst[2 * lane + 1] = src[2 * lane + 1];
   }
 
-  // ---- query heads of the group, scaled to log2 units ----
+  // ---- every load of the first phase goes out before any wait: the query heads, the
+  // quantized partials' first chunk (the merge's inputs, written by the decode launch before
+  // this one) and the first tile's window rows ----
+  constexpr int NQ = GP * kHeadDim / kWinThreads;     // query elements and merge outputs per thread
   const T* qb = reinterpret_cast<const T*>(p.q) + ((int64_t)b * p.heads_q + (int64_t)kvh * G) * kHeadDim;
-  for (int idx = threadIdx.x; idx < GP * kHeadDim; idx += kWinThreads)
-    qs[idx / kHeadDim][idx % kHeadDim] = idx < G * kHeadDim ? Elem<T>::get(qb, idx) * p.score_scale : 0.0f;
-
-  float o[GP][8];
+  float qv[NQ];
 #pragma unroll
-  for (int g = 0; g < GP; ++g)
-#pragma unroll
-    for (int c = 0; c < 8; ++c) o[g][c] = 0.0f;
-  float mrun[HW], lrun[HW];
-#pragma unroll
-  for (int k = 0; k < HW; ++k) {
-    mrun[k] = -__builtin_inff();
-    lrun[k] = 0.0f;
+  for (int j = 0; j < NQ; ++j) {
+    const int idx = threadIdx.x + j * kWinThreads;
+    const float x = Elem<T>::get(qb, min(idx, G * kHeadDim - 1));   // in range for every lane
+    qv[j] = idx < G * kHeadDim ? x : 0.0f;
   }
-  __syncthreads();
-
-  for (int t0 = 0; t0 < nf; t0 += kTile) {
-    Raw8<T> kr[NI], vr[NI];
-    bool ok[NI];
+  // chunk 0 of merge output idx = threadIdx.x + j * threads (at 16 query heads per KV head the
+  // registers that would hold them, and the first tile, through the query staging cost
+  // occupancy: those load at the merge and in the tile loop)
+  constexpr bool kPre = GP <= 8;
+  constexpr int NP = kPre ? NQ : 1;
+  float pm0[NP], pl0[NP], po0[NP];
+  auto load_chunk0 = [&](int j, float& m0, float& l0, float& o0) {
+    const int idx = threadIdx.x + j * kWinThreads;
+    const int64_t prow = (int64_t)b * p.heads_q + (int64_t)kvh * G + min(idx / kHeadDim, G - 1);
+    m0 = p.ws_ml[prow * p.chunks * 2];
+    l0 = p.ws_ml[prow * p.chunks * 2 + 1];
+    o0 = p.ws_o[prow * p.chunks * kHeadDim + idx % kHeadDim];
+  };
+  if constexpr (kPre) {
+#pragma unroll
+    for (int j = 0; j < NQ; ++j) load_chunk0(j, pm0[j], pl0[j], po0[j]);
+  }
+  Raw8<T> kr[NI], vr[NI];
+  bool ok[NI];
+  auto load_tile = [&](int t0) {
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
       const int t = t0 + (wave * NI + i) * 4 + tg;
@@ -165,6 +176,30 @@ __global__ __launch_bounds__(kWinThreads) void window_kernel(DecodeParams p, Win
         vr[i] = zero8<T>();
       }
     }
+  };
+  if constexpr (kPre) load_tile(0);
+  // ---- query heads of the group, scaled to log2 units ----
+#pragma unroll
+  for (int j = 0; j < NQ; ++j) {
+    const int idx = threadIdx.x + j * kWinThreads;
+    qs[idx / kHeadDim][idx % kHeadDim] = qv[j] * p.score_scale;
+  }
+
+  float o[GP][8];
+#pragma unroll
+  for (int g = 0; g < GP; ++g)
+#pragma unroll
+    for (int c = 0; c < 8; ++c) o[g][c] = 0.0f;
+  float mrun[HW], lrun[HW];
+#pragma unroll
+  for (int k = 0; k < HW; ++k) {
+    mrun[k] = -__builtin_inff();
+    lrun[k] = 0.0f;
+  }
+  __syncthreads();
+
+  for (int t0 = 0; t0 < nf; t0 += kTile) {
+    if (!kPre || t0 > 0) load_tile(t0);
     // scores: lane column g keeps head g's score of its row's token
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
@@ -269,13 +304,24 @@ __global__ __launch_bounds__(kWinThreads) void window_kernel(DecodeParams p, Win
   __syncthreads();
 
   // ---- merge with the quantized partials and write the output ----
-  for (int idx = threadIdx.x; idx < G * kHeadDim; idx += kWinThreads) {
+#pragma unroll
+  for (int j = 0; j < NQ; ++j) {
+    const int idx = threadIdx.x + j * kWinThreads;
+    if (idx >= G * kHeadDim) break;
     const int g = idx / kHeadDim, ch = idx % kHeadDim;
     const int64_t prow = (int64_t)b * p.heads_q + (int64_t)kvh * G + g;
     const float* ml = p.ws_ml + prow * p.chunks * 2;
+    float m0, l0, o0;
+    if constexpr (kPre) {
+      m0 = pm0[j];
+      l0 = pl0[j];
+      o0 = po0[j];
+    } else {
+      load_chunk0(j, m0, l0, o0);
+    }
     const float mw = ml_s[g][0];
-    float M = mw;
-    for (int c = 0; c < p.chunks; ++c) M = fmaxf(M, ml[2 * c]);
+    float M = fmaxf(mw, m0);
+    for (int c = 1; c < p.chunks; ++c) M = fmaxf(M, ml[2 * c]);
     float L = 0.0f, O = 0.0f;
     if (M != -__builtin_inff()) {
       if (mw != -__builtin_inff()) {
@@ -283,7 +329,12 @@ __global__ __launch_bounds__(kWinThreads) void window_kernel(DecodeParams p, Win
         L = ml_s[g][1] * f;
         O = (((red[0][g][ch] + red[1][g][ch]) + red[2][g][ch]) + red[3][g][ch]) * f;
       }
-      for (int c = 0; c < p.chunks; ++c) {
+      if (m0 != -__builtin_inff()) {
+        const float f = exp2f(m0 - M);
+        L = __builtin_fmaf(l0, f, L);
+        O = __builtin_fmaf(o0, f, O);
+      }
+      for (int c = 1; c < p.chunks; ++c) {
         const float mc = ml[2 * c];
         if (mc != -__builtin_inff()) {
           const float f = exp2f(mc - M);
