@@ -97,3 +97,62 @@ def test_graph_replays_match_eager_and_oracle():
     ref = oracle.decode_attention(kp, vp, d["q"], d["bt"], d["seq"], t_inv_t=d["t_inv"], bits_k=2, bits_v=2)
     err = row_rel_err(eager_out.cpu().numpy(), ref)
     assert err.max() <= 2e-3, err.max()
+
+
+def test_graph_replays_of_the_step_with_query_operand_image():
+    """kvq_decode_step with its full workspace on a split decode: the first launch appends
+    the new tokens and writes the query-operand image into the workspace, and the decode and
+    merge launches read it.  Captured once and replayed with the workspace scribbled over in
+    between, every replay equals the eager step bit for bit, and the eager step matches the
+    oracle."""
+    d = _setup([200, 2900, 64, 1])
+    dev = torch.device("cuda")
+    H = d["H"]
+    cache = api.KVCache(d["kp"].shape[0], H, 2, 2, k_pages=torch.from_numpy(d["kp"]).to(dev),
+                        v_pages=torch.from_numpy(d["vp"]).to(dev))
+    kp0, vp0 = cache.k_pages.clone(), cache.v_pages.clone()
+    t_k = torch.from_numpy(d["t_k"]).to(torch.bfloat16).to(dev)
+    t_inv = torch.from_numpy(d["t_inv"]).to(dev)
+    knew = torch.from_numpy(d["k_new"]).to(torch.bfloat16).to(dev)
+    vnew = torch.from_numpy(d["v_new"]).to(torch.bfloat16).to(dev)
+    slots = torch.from_numpy(d["new_slots"]).to(dev)
+    bt = torch.from_numpy(d["bt"]).to(dev)
+    seq = torch.from_numpy(d["seq"]).to(dev)
+    q = torch.from_numpy(d["q"]).to(torch.bfloat16).to(dev)
+    msl = int(d["seq"].max())
+    B, Hq = q.shape[0], q.shape[1]
+    need = api.decode_step_workspace_bytes(cache, B, Hq, msl)
+    assert need > api.decode_workspace_bytes(cache, B, Hq, msl) > 0, "split decode with an operand image"
+    ws = torch.empty(need, dtype=torch.uint8, device=dev)
+    out = torch.empty((B, Hq, 128), dtype=torch.float32, device=dev)
+
+    def step():
+        api.kvq_decode_step(cache, q, knew, vnew, slots, bt, seq, msl, t_k=t_k, t_k_inv_t=t_inv, out=out,
+                            workspace=ws)
+
+    step()
+    torch.cuda.synchronize()
+    eager_out = out.clone()
+    eager_k, eager_v = cache.k_pages.clone(), cache.v_pages.clone()
+
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    for r in range(4):
+        cache.k_pages.copy_(kp0)
+        cache.v_pages.copy_(vp0)
+        out.fill_(float("nan"))
+        ws.fill_(0xAB)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(cache.k_pages, eager_k), f"replay {r}: K pool differs from eager"
+        assert torch.equal(cache.v_pages, eager_v), f"replay {r}: V pool differs from eager"
+        assert torch.equal(out, eager_out), f"replay {r}: output differs from eager"
+
+    kp, vp = d["kp"].copy(), d["vp"].copy()
+    oracle.append(kp, vp, d["k_new"], d["v_new"], d["new_slots"], t_k=d["t_k"].astype(np.float32),
+                  bits_k=2, bits_v=2)
+    ref = oracle.decode_attention(kp, vp, d["q"], d["bt"], d["seq"], t_inv_t=d["t_inv"], bits_k=2, bits_v=2)
+    err = row_rel_err(eager_out.cpu().numpy(), ref)
+    assert err.max() <= 2e-3, err.max()
