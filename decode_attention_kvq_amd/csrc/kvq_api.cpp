@@ -163,11 +163,13 @@ kvq_status check_window(const kvq_cache_desc* cache, const kvq_window_desc* w, b
     return fail(KVQ_ERR_INVALID_ARG, "window sizes must satisfy sink >= 0, keep >= 0, flush >= 1");
   if ((int64_t)w->sink + w->keep + w->flush > KVQ_WINDOW_MAX_SLOTS)
     return fail(KVQ_ERR_UNSUPPORTED, "sink + keep + flush exceeds KVQ_WINDOW_MAX_SLOTS");
+  // the window kernel addresses a row's elements with 32-bit offsets
+  if (cache && ((int64_t)w->sink + w->keep + w->flush) * cache->num_kv_heads * 128 > 0xFFFFFFFFLL)
+    return fail(KVQ_ERR_UNSUPPORTED, "(sink + keep + flush) * num_kv_heads * 128 must be < 2^32");
   if (!valid_dtype(w->dtype)) return fail(KVQ_ERR_INVALID_ARG, "unknown window dtype");
   if (w->num_rows < 0) return fail(KVQ_ERR_INVALID_ARG, "num_rows must be >= 0");
   if (need_data && (w->num_rows < 1 || !w->k_win || !w->v_win))
     return fail(KVQ_ERR_INVALID_ARG, "window tensors must be non-null with num_rows >= 1");
-  (void)cache;
   *shape = kvq::WindowShape{w->sink, w->keep, w->flush};
   return KVQ_OK;
 }

@@ -160,17 +160,25 @@ __global__ __launch_bounds__(kWinThreads) void window_kernel(DecodeParams p, Win
   }
   Raw8<T> kr[NI], vr[NI];
   bool ok[NI];
+  // ring slot of the first recent position (uniform): recent position len - nr + r sits r
+  // slots later, wrapped once at most (r < nr <= keep + flush), so no token needs a division
+  const int ring = ws.keep + ws.flush;
+  const int srec = ws.sink + max(len - nr - ws.sink, 0) % ring;
   auto load_tile = [&](int t0) {
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
       const int t = t0 + (wave * NI + i) * 4 + tg;
       ok[i] = t < nf;
       if (ok[i]) {
-        const int pos = t < ns ? t : len - nr + (t - ns);
+        const int r = t - ns;
+        const int pos = t < ns ? t : len - nr + r;
         const bool fresh = has_new && pos == len - 1;
-        const int64_t off = (int64_t)window_slot(pos, ws) * tstride + c0;
-        kr[i] = load8<T>(fresh ? kn + c0 : kw + off);
-        vr[i] = load8<T>(fresh ? vn + c0 : vw + off);
+        const int wrapped = srec + r >= ws.sink + ring ? srec + r - ring : srec + r;
+        // 32-bit element offsets within the row (a row spans window_width * heads_kv * 128
+        // elements)
+        const uint32_t off = fresh ? (uint32_t)c0 : (uint32_t)(t < ns ? t : wrapped) * (uint32_t)tstride + c0;
+        kr[i] = load8<T>((fresh ? kn : kw) + off);
+        vr[i] = load8<T>((fresh ? vn : vw) + off);
       } else {
         kr[i] = zero8<T>();
         vr[i] = zero8<T>();

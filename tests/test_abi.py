@@ -233,6 +233,9 @@ def test_window_argument_checks(lib):
     assert attn(w=_win(flush=0)) == -1
     assert attn(w=_win(sink=-1)) == -1
     assert attn(w=_win(sink=40000, keep=30000)) == -2
+    # a window row of 2^32 or more elements is refused (32-bit offsets inside a row)
+    assert attn(d=_desc(num_kv_heads=16384), Hq=16384, w=_win(sink=1000, keep=1000, flush=100)) == -2
+    assert attn(d=_desc(num_kv_heads=16384), Hq=16384, w=_win(sink=1000, keep=1000, flush=47)) == -3
     assert attn(w=_win(dtype=7)) == -1
     assert attn(w=_win(k_win=None)) == -1
     assert attn(w=_win(num_rows=0)) == -1
