@@ -77,13 +77,18 @@ def round_bf16(x: np.ndarray) -> np.ndarray:
 
 
 def calibrate_key_transform(k_cal: np.ndarray, q_cal: np.ndarray, gamma: float = DEFAULT_GAMMA,
-                            hadamard: bool = True, store_bf16: bool = True):
+                            hadamard: bool = True, store_bf16: bool = True, store_f16: bool = False):
     """Returns (T, T_inv_T) for one KV head as fp32 arrays [d, d].
 
-    T is what the write path applies (k' = k T); when store_bf16 it holds bf16 values.
+    T is what the write path applies (k' = k T); when store_f16 it holds fp16 values (for
+    fp16 inputs, whose T is passed as fp16), else when store_bf16 bf16 values.
     T_inv_T = (T^-1)^T of exactly that stored T, for the read path (q' = q T^-T)."""
     t = wush(*key_statistics(k_cal, q_cal), gamma=gamma, hadamard=hadamard)
-    t_store = np.ascontiguousarray(round_bf16(t) if store_bf16 else t.astype(np.float32))
+    if store_f16:
+        t_store = np.asarray(t, dtype=np.float64).astype(np.float16).astype(np.float32)
+    else:
+        t_store = round_bf16(t) if store_bf16 else t.astype(np.float32)
+    t_store = np.ascontiguousarray(t_store)
     t_inv_t = np.ascontiguousarray(np.linalg.inv(t_store.astype(np.float64)).T, dtype=np.float32)
     return t_store, t_inv_t
 

@@ -118,3 +118,14 @@ def test_package_calibration_matches_reference(gamma):
         tb = wush.bf16_round(t_ref)
         assert np.mean(ts != tb) < 1e-3           # a rounding tie may fall either way
         assert np.allclose(tinv, wush.inverse_transpose(ts), rtol=1e-6, atol=1e-7)
+
+
+def test_fp16_stored_transform():
+    """For fp16 inputs the transform is stored as fp16 values (what the write path receives),
+    and T_inv_T is the inverse transpose of exactly that stored matrix."""
+    k_cal, q_cal = synth.calibration_set(1, 0, 4)
+    t_ref = wush.wush_transform(k_cal, q_cal)
+    ts, tinv = calib.calibrate_key_transform(k_cal, q_cal, store_f16=True)
+    assert np.array_equal(ts.astype(np.float16).astype(np.float32), ts)       # fp16 values
+    assert np.max(np.abs(ts - t_ref)) <= np.abs(t_ref).max() * 2.0 ** -11      # rounded, not rescaled
+    assert np.allclose(tinv, wush.inverse_transpose(ts), rtol=1e-6, atol=1e-7)

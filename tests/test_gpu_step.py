@@ -43,7 +43,7 @@ def _setup(rng, B, H, G, lens, bits, quant, dtype, transform, config=1):
         ts, tis = [], []
         for h in range(H):
             kc, qc = synth.calibration_set(config, h, G)
-            a, c = calib.calibrate_key_transform(kc, qc, store_bf16=(dtype == "bf16"))
+            a, c = calib.calibrate_key_transform(kc, qc, store_bf16=(dtype == "bf16"), store_f16=(dtype == "f16"))
             ts.append(a)
             tis.append(c)
         t, tinv = np.stack(ts).astype(np.float32), np.stack(tis).astype(np.float32)

@@ -22,7 +22,7 @@ def _transforms(H, G, dtype):
     ts, tis = [], []
     for h in range(H):
         kc, qc = synth.calibration_set(1, h, G)
-        t, ti = calib.calibrate_key_transform(kc, qc, store_bf16=(dtype == "bf16"))
+        t, ti = calib.calibrate_key_transform(kc, qc, store_bf16=(dtype == "bf16"), store_f16=(dtype == "f16"))
         ts.append(synth.to_dtype(t, dtype))
         tis.append(np.ascontiguousarray(np.linalg.inv(synth.to_dtype(t, dtype).astype(np.float64)).T, np.float32))
     return np.stack(ts), np.stack(tis)
