@@ -282,3 +282,79 @@ def test_full_size_decode_sampled(name):
         ref = oracle.decode_attention(kp, vp, q[b:b + 1], bt[b:b + 1], seq[b:b + 1], t_inv_t=tinv,
                                       bits_k=w.bits_k, bits_v=w.bits_v)
         assert row_rel_err(got[b:b + 1], ref).max() <= TOL, b
+
+
+def _compact(bt, seq, num_pages):
+    """The block table and lengths with every page id outside [0, num_pages) taken out:
+    the tokens such a page would hold contribute nothing, so attention over a sequence is
+    attention over the tokens of its valid pages."""
+    bt_c = np.zeros_like(bt)
+    seq_c = np.zeros_like(seq)
+    for b in range(bt.shape[0]):
+        n = int(seq[b])
+        keep_pages, tokens = [], 0
+        for j in range(-(-n // 64)):
+            pid = int(bt[b, j])
+            if 0 <= pid < num_pages:
+                keep_pages.append(pid)
+                tokens += min(64, n - 64 * j)
+        # a kept partial page must stay last: only the sequence's own last page is partial
+        bt_c[b, :len(keep_pages)] = keep_pages
+        seq_c[b] = tokens
+    return bt_c, seq_c
+
+
+def test_invalid_page_ids_contribute_nothing():
+    """Page ids outside [0, num_pages) (negative, or past the pool) in the middle of a
+    sequence, on its partial last page and in a sequence split over several workgroups:
+    the output equals the oracle's attention over the valid pages' tokens."""
+    rng = np.random.default_rng(41)
+    B, H, G, bits = 4, 2, 4, (2, 2)
+    seq = np.array([1300, 200, 5000, 70], np.int32)
+    kp, vp, bt = _oracle_cache(rng, B, H, seq, bits)
+    num_pages = kp.shape[0]
+    bt = bt.copy()
+    bt[0, 3] = -1
+    bt[0, 10] = num_pages + 7
+    bt[1, 3] = -5                                       # the partial last page (200 = 3 * 64 + 8)
+    bt[2, [0, 17, 40, 78]] = [-1, num_pages, -2, num_pages + 1]   # 78: the partial last page
+    q = synth.to_dtype(rng.standard_normal((B, H * G, 128)).astype(np.float32), "bf16")
+    got = _gpu_decode(kp, vp, q, bt, seq, bits, q_dtype="bf16")
+    bt_c, seq_c = _compact(bt, seq, num_pages)
+    assert seq_c[1] == 192 and seq_c[2] == 5000 - 64 * 3 - 8
+    ref = oracle.decode_attention(kp, vp, q, bt_c, seq_c, bits_k=bits[0], bits_v=bits[1])
+    err = row_rel_err(got, ref)
+    assert err.max() <= TOL, err.max()
+
+
+def test_invalid_page_ids_in_runs_of_128_pages():
+    """A launch whose waves walk 128 pages each (batch 32 x 8 KV heads x 64K tokens: the
+    page ids of a wave sit in two registers): two sampled sequences have real pages, with
+    invalid ids at run positions below and above 64; every other sequence has only invalid
+    page ids and gives zeros."""
+    rng = np.random.default_rng(43)
+    B, H, G, bits, n = 32, 8, 4, (2, 2), 65536
+    pages = n // 64
+    picks = [5, 22]
+    num_pages = len(picks) * pages
+    kp = synth.random_packed_pool(rng, num_pages, H, bits[0])
+    vp = synth.random_packed_pool(rng, num_pages, H, bits[1])
+    bt = np.full((B, pages), -1, np.int32)
+    for i, b in enumerate(picks):
+        bt[b] = rng.permutation(pages).astype(np.int32) + i * pages
+    # 128-page runs: run r of a sequence covers pages 128 r .. 128 r + 127; positions 64 and
+    # up within a run sit in the second register
+    bt[5, [3, 64, 127, 128 + 70, 1023]] = [-1, num_pages, -3, num_pages + 100, -1]
+    bt[22, [200, 255, 600]] = [num_pages + 2, -1, -7]
+    seq = np.full(B, n, np.int32)
+    cache = api.KVCache(num_pages, H, bits[0], bits[1])
+    ws = api.decode_workspace_bytes(cache, B, H * G, n)
+    assert ws > 0
+    q = synth.to_dtype(rng.standard_normal((B, H * G, 128)).astype(np.float32), "bf16")
+    got = _gpu_decode(kp, vp, q, bt, seq, bits, q_dtype="bf16")
+    others = [b for b in range(B) if b not in picks]
+    assert np.all(got[others] == 0)
+    bt_c, seq_c = _compact(bt[picks], seq[picks], num_pages)
+    ref = oracle.decode_attention(kp, vp, q[picks], bt_c, seq_c, bits_k=bits[0], bits_v=bits[1])
+    err = row_rel_err(got[picks], ref)
+    assert err.max() <= TOL, err.max()
