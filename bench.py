@@ -16,7 +16,9 @@ dominant kernel, the decode: algorithmic bytes per launch over its average launc
 8 TB/s.  `cpu_baseline` is the CPU oracle's decode timed on a bounded sample of sequences
 of the same shape, on one thread and on all available cores.  `step_ms_p10_p50_p90` spreads nine more replays of the timed graph;
 `reference_bandwidth` is what plain torch kernels reach on the same GPU (a 1 GiB read and
-a 1 GiB copy), for context.
+a 1 GiB copy), for context; it runs right before the step's warm-up replay, so that the timed
+replay follows load rather than idle (after idle the clocks take a few milliseconds of load
+to settle).
 """
 from __future__ import annotations
 
@@ -43,6 +45,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=400)
     ap.add_argument("--workload", default="qwen3-8b-b64-16k")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--reference-ms", type=float, default=60.0,
+                    help="how long the reference-bandwidth probe runs (directly before the timed replays)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--extra", action="store_true", help="also time the other workloads")
     ap.add_argument("--prefill-only", metavar="WORKLOAD", default=None,
@@ -106,13 +110,14 @@ def setup_decode(w, torch, api, calib, synth, dev):
                 new_slots=new_slots, ws=ws, out=out)
 
 
-def time_steps(w, s, torch, api, steps, warmup):
+def time_steps(w, s, torch, api, steps, warmup, before=None):
     """Times the step, kvq_decode_step (the batch's new tokens appended, then every sequence
     decoded), as one HIP-graph replay of `steps` consecutive steps (captured from the
     library calls, which launch on torch's current stream), after one replay of a graph of
     `warmup` steps, so the host's per-call and per-replay cost does not pace the GPU.  HIP
     events on the launch stream bracket the timed replay.  The append and the decode kernel
-    alone are timed the same way.  Returns ms per step of each."""
+    alone are timed the same way.  `before` runs directly before the step's warm-up replay.
+    Returns ms per step of each."""
 
     def append():
         api.kvq_quantize_append(s["cache"], s["knew"], s["vnew"], s["new_slots"], t_k=s["t_k"])
@@ -127,7 +132,7 @@ def time_steps(w, s, torch, api, steps, warmup):
 
     step()                                   # first call (library load) outside the graphs
     torch.cuda.synchronize()
-    ms_step, wall_step, more = graph_time(torch, step, steps, warmup, extra_replays=9)
+    ms_step, wall_step, more = graph_time(torch, step, steps, warmup, extra_replays=9, before=before)
     ms_app, _ = graph_time(torch, append, steps, warmup)
     ms_dec, _ = graph_time(torch, decode, steps, warmup)
     return dict(step=ms_step, wall=wall_step, append=ms_app, decode=ms_dec, step_replays=[ms_step] + more)
@@ -158,15 +163,23 @@ def time_decode_from_hbm(w, s, torch, api, steps, warmup):
     return ms, copies
 
 
-def reference_bandwidth(torch, dev, nbytes=1 << 30, reps=10):
+def reference_bandwidth(torch, dev, nbytes=1 << 30, run_ms=60.0):
     """What plain torch kernels reach on this GPU, as an achievable-bandwidth reference: the
-    sum of a 1 GiB fp32 tensor (read) and a 1 GiB device copy (read + write), in GB/s."""
+    sum of a 1 GiB fp32 tensor (read) and a 1 GiB device copy (read + write), in GB/s, each
+    repeated back to back for about run_ms / 2.  It runs directly before the timed replays of
+    the step: after idle the GPU needs some tens of milliseconds of load before its clocks
+    settle, and this probe is that load (the tensors stay in torch's cache, so no free sits
+    between it and the replays)."""
     src = torch.ones(nbytes // 4, dtype=torch.float32, device=dev)
     dst = torch.empty_like(src)
     out = {}
     for name, fn, moved in (("read_sum", lambda: src.sum(), nbytes), ("copy", lambda: dst.copy_(src), 2 * nbytes)):
         fn()
         torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        fn()
+        torch.cuda.synchronize()
+        reps = max(10, int(run_ms / 2 / max((time.perf_counter() - t0) * 1e3, 1e-3)))
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
         for _ in range(reps):
@@ -174,17 +187,18 @@ def reference_bandwidth(torch, dev, nbytes=1 << 30, reps=10):
         e1.record()
         torch.cuda.synchronize()
         out[name + "_GB_s"] = moved / (e0.elapsed_time(e1) / reps * 1e-3) / 1e9
+        out[name + "_reps"] = reps
     del src, dst
-    torch.cuda.empty_cache()
     return out
 
 
-def graph_time(torch, fn, steps, warmup, extra_replays=0):
+def graph_time(torch, fn, steps, warmup, extra_replays=0, before=None):
     """ms per call of fn: one replay of a HIP graph of `steps` calls (captured from the
     library calls on torch's current stream) after one replay of a graph of `warmup`
     calls, bracketed by HIP events on the launch stream; also the host wall time.  With
     extra_replays, the timed graph is replayed that many more times and the per-call times
-    of those replays are returned too."""
+    of those replays are returned too.  `before`, if given, runs once the graphs are
+    captured, directly before the warm-up replay."""
 
     def capture(count):
         g = torch.cuda.CUDAGraph()
@@ -195,6 +209,8 @@ def graph_time(torch, fn, steps, warmup, extra_replays=0):
 
     gw, gt = capture(max(warmup, 1)), capture(steps)
     torch.cuda.synchronize()
+    if before is not None:
+        before()
     gw.replay()
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -402,7 +418,9 @@ def main():
         return
     w = synth.WORKLOADS[args.workload]
     s = setup_decode(w, torch, api, calib, synth, dev)
-    t = time_steps(w, s, torch, api, args.steps, args.warmup)
+    ref = {}
+    t = time_steps(w, s, torch, api, args.steps, args.warmup,
+                   before=lambda: ref.update(reference_bandwidth(torch, dev, run_ms=args.reference_ms)))
     cached = w.batch * w.seq_len
     dbytes = decode_algorithmic_bytes(w, w.batch, w.seq_len)
     achieved = dbytes / (t["decode"] * 1e-3)
@@ -432,7 +450,7 @@ def main():
         extra = {w.name + "-window": time_window(w, s, torch, api, args.steps, args.warmup)}
     del s
     torch.cuda.empty_cache()
-    rec["reference_bandwidth"] = reference_bandwidth(torch, dev)
+    rec["reference_bandwidth"] = ref
     if args.extra:
         for name in ("qwen3-8b-b1-16k", "long-b16-128k-quest", "qwen3-8b-b64-16k-3bit"):
             w2 = synth.WORKLOADS[name]
