@@ -210,10 +210,11 @@ def test_dequant_bit_exact(bits, which):
     assert np.array_equal(got.view(np.uint32), ref.view(np.uint32))
 
 
-@pytest.mark.parametrize("bits", [4, 2])
+@pytest.mark.parametrize("bits", [4, 2, 3])
 def test_bulk_prefill_full_size_sampled(bits):
-    """Bulk prefill: 8 KV heads x 32768 tokens, bf16, dense transform on the matrix cores.
-    The oracle re-encodes a seeded sample of 1024 tokens (all heads)."""
+    """Bulk prefill: 8 KV heads x 32768 tokens, bf16, dense transform on the matrix cores
+    (3-bit: the two-plane kernel).  The oracle re-encodes a seeded sample of 1024 tokens
+    (all heads)."""
     w = synth.WORKLOADS["prefill-8x32k-%dbit" % bits]
     n, H = w.seq_len, w.heads_kv
     dev = torch.device("cuda")
