@@ -1,9 +1,9 @@
 """Host-side (offline) calibration of the per-KV-head key and value transforms.
 
 Follows "WUSH-KV: KV Cache Quantization with Data-Adaptive Transforms":
-  §3    the transform comes from the second-order statistics of both factors of the
-        product: the Gram matrix M of the quantized tensor (the cached keys) and the
-        Hessian H of its partner; damping makes both positive definite; a scalar keeps
+  §3    the transform is built from two covariance-type matrices, one per operand of
+        the product: the Gram matrix M of the quantized tensor (the cached keys) and
+        the Hessian H of its partner; damping makes both positive definite; a scalar keeps
         the Frobenius norm (exactly when undamped); rescaling M or H changes nothing.
   §4.2  one key transform per KV head, with a local surrogate Hessian.  For keys the
         partner is the query: a key error e moves the logit of query q by q.e, so
