@@ -84,3 +84,25 @@ def test_window_spanning_many_tiles():
             hk[b, p], hv[b, p] = kw[b, slot], vw[b, slot]
     ref = oracle.window_attention(kp, vp, q, bt, lens, hk, hv, sink, keep, flush)
     assert row_rel_err(out.cpu().numpy(), ref).max() <= TOL
+
+
+def test_long_sequences_merge_over_many_chunk_blocks():
+    """Two sequences of 1,000,000 and 300,000 tokens, 2 KV heads: the launch splits every
+    sequence into 127 chunks, so the merge runs over a full block of 64 chunks and a partial
+    one of 63, and for the shorter sequence the second block holds no tokens at all."""
+    rng = np.random.default_rng(1_000_000)
+    B, H, G = 2, 2, 4
+    seq = np.array([1_000_000, 300_000], np.int32)
+    pps = -(-int(seq.max()) // 64)
+    num_pages = B * pps
+    kp = synth.random_packed_pool(rng, num_pages, H, 2)
+    vp = synth.random_packed_pool(rng, num_pages, H, 2)
+    bt = synth.shuffled_block_table(B, pps, num_pages, rng)
+    q = synth.to_dtype(rng.standard_normal((B, H * G, 128)).astype(np.float32), "bf16")
+    cache = api.KVCache(num_pages, H, 2, 2, k_pages=torch.from_numpy(kp).cuda(), v_pages=torch.from_numpy(vp).cuda())
+    assert api.decode_workspace_bytes(cache, B, H * G, int(seq.max())) >= B * H * G * 127 * (128 + 2) * 4
+    out = api.kvq_decode_attn(cache, torch.from_numpy(q).to(torch.bfloat16).cuda(), torch.from_numpy(bt).cuda(),
+                              torch.from_numpy(seq).cuda(), int(seq.max()))
+    torch.cuda.synchronize()
+    ref = oracle.decode_attention(kp, vp, q, bt, seq, bits_k=2, bits_v=2)
+    assert row_rel_err(out.cpu().numpy(), ref).max() <= TOL
