@@ -264,7 +264,7 @@ def test_qwen3_8b_b1_16k_full():
     assert row_rel_err(got, ref).max() <= TOL
 
 
-@pytest.mark.parametrize("name", ["qwen3-8b-b64-16k", "long-b16-128k-quest"])
+@pytest.mark.parametrize("name", ["qwen3-8b-b64-16k", "long-b16-128k-quest", "qwen3-8b-b64-16k-3bit"])
 def test_full_size_decode_sampled(name):
     """Full-size caches of random codes in the launch configuration the benchmark times;
     the oracle recomputes a seeded sample of sequences (all their query heads)."""
