@@ -15,10 +15,10 @@ dominant kernel, the decode: algorithmic bytes per launch over its average launc
 (HIP events on the launch stream around the timed replay of a decode-only graph) against
 8 TB/s.  `cpu_baseline` is the CPU oracle's decode timed on a bounded sample of sequences
 of the same shape, on one thread and on all available cores.  `step_ms_p10_p50_p90` spreads nine more replays of the timed graph;
-`reference_bandwidth` is what plain torch kernels reach on the same GPU (a 1 GiB read and
-a 1 GiB copy), for context; it runs right before the step's warm-up replay, so that the timed
-replay follows load rather than idle (after idle the clocks take a few milliseconds of load
-to settle).
+`reference_bandwidth` is what plain torch kernels reach on the same GPU (a 1 GiB copy and a
+sum over the KV-cache pools), for context; it runs right before the step's warm-up replay, so
+that the timed replay follows load rather than idle (after idle the clocks take a few
+milliseconds of load to settle) and finds the cache's address translations warm.
 """
 from __future__ import annotations
 
@@ -163,17 +163,25 @@ def time_decode_from_hbm(w, s, torch, api, steps, warmup):
     return ms, copies
 
 
-def reference_bandwidth(torch, dev, nbytes=1 << 30, run_ms=60.0):
-    """What plain torch kernels reach on this GPU, as an achievable-bandwidth reference: the
-    sum of a 1 GiB fp32 tensor (read) and a 1 GiB device copy (read + write), in GB/s, each
-    repeated back to back for about run_ms / 2.  It runs directly before the timed replays of
-    the step: after idle the GPU needs some tens of milliseconds of load before its clocks
-    settle, and this probe is that load (the tensors stay in torch's cache, so no free sits
-    between it and the replays)."""
+def reference_bandwidth(torch, dev, read_tensors, nbytes=1 << 30, run_ms=60.0):
+    """What plain torch kernels reach on this GPU, as an achievable-bandwidth reference: a
+    1 GiB device copy (read + write), then a sum over `read_tensors` (the KV-cache pools, the
+    very bytes the decode reads, viewed as fp32), in GB/s, each repeated back to back for
+    about run_ms / 2.  It runs directly before the timed replays of the step: after idle the
+    GPU needs some tens of milliseconds of load before its clocks settle, and reading the
+    cache last leaves its address translations warm (the copy's buffers stay in torch's
+    cache, so no free sits between the probe and the replays)."""
     src = torch.ones(nbytes // 4, dtype=torch.float32, device=dev)
     dst = torch.empty_like(src)
+    views = [t.view(torch.float32).view(-1) for t in read_tensors]
+    read_bytes = sum(v.numel() * 4 for v in views)
+
+    def read_sum():
+        for v in views:
+            v.sum()
+
     out = {}
-    for name, fn, moved in (("read_sum", lambda: src.sum(), nbytes), ("copy", lambda: dst.copy_(src), 2 * nbytes)):
+    for name, fn, moved in (("copy", lambda: dst.copy_(src), 2 * nbytes), ("cache_read_sum", read_sum, read_bytes)):
         fn()
         torch.cuda.synchronize()
         t0 = time.perf_counter()
@@ -188,6 +196,7 @@ def reference_bandwidth(torch, dev, nbytes=1 << 30, run_ms=60.0):
         torch.cuda.synchronize()
         out[name + "_GB_s"] = moved / (e0.elapsed_time(e1) / reps * 1e-3) / 1e9
         out[name + "_reps"] = reps
+    out["cache_read_bytes"] = read_bytes
     del src, dst
     return out
 
@@ -420,7 +429,8 @@ def main():
     s = setup_decode(w, torch, api, calib, synth, dev)
     ref = {}
     t = time_steps(w, s, torch, api, args.steps, args.warmup,
-                   before=lambda: ref.update(reference_bandwidth(torch, dev, run_ms=args.reference_ms)))
+                   before=lambda: ref.update(reference_bandwidth(torch, dev, (s["cache"].k_pages, s["cache"].v_pages),
+                                                                 run_ms=args.reference_ms)))
     cached = w.batch * w.seq_len
     dbytes = decode_algorithmic_bytes(w, w.batch, w.seq_len)
     achieved = dbytes / (t["decode"] * 1e-3)
