@@ -220,6 +220,42 @@ def decode_attention(k_pool, v_pool, q, block_table, seq_lens, t_inv_t=None, bit
     return (out, lse) if return_lse else out
 
 
+def decode_step(k_pool, v_pool, q, block_table, seq_lens, k_new, v_new, t_inv_t=None, bits_k=2,
+                bits_v=2, sm_scale=None):
+    """A decode step whose new token takes part at full precision ([W] §4.4: a new entry is
+    used for attention before it is quantized), fp64 output.
+
+    For each sequence b with L = seq_lens[b] > 0: softmax attention over positions
+    [0, L - 1) dequantized from the cache (as decode_attention, with the compensated query)
+    and the new token's own key k_new[b] and value v_new[b] ([B, H, 128]); the new token's
+    score is sm_scale q . k_new, the product that q' . k' gives under the key transform.
+    Rows of sequences with L = 0 are 0.  Pinned against torch fp64 attention over the
+    cache's dequantized keys and values followed by the new row, with and without a key
+    transform (tests/test_oracle_attention.py)."""
+    sl = np.ascontiguousarray(seq_lens, dtype=np.int32)
+    out_q, lse_q = decode_attention(k_pool, v_pool, q, block_table, np.maximum(sl - 1, 0).astype(np.int32),
+                                    t_inv_t=t_inv_t, bits_k=bits_k, bits_v=bits_v, sm_scale=sm_scale,
+                                    return_lse=True)
+    if sm_scale is None:
+        sm_scale = 1.0 / np.sqrt(HEAD_DIM)
+    q64 = _f32(q).astype(np.float64)
+    kn = _f32(k_new).astype(np.float64)
+    vn = _f32(v_new).astype(np.float64)
+    B, Hq, _ = q64.shape
+    G = Hq // k_pool.shape[1]
+    out = np.zeros((B, Hq, HEAD_DIM), np.float64)
+    for b in range(B):
+        if sl[b] <= 0:
+            continue
+        for hq in range(Hq):
+            s = float(sm_scale) * float(q64[b, hq] @ kn[b, hq // G])
+            m = max(s, float(lse_q[b, hq]))
+            w_cache = np.exp(lse_q[b, hq] - m)          # 0 when the cache part is empty
+            w_new = np.exp(s - m)
+            out[b, hq] = (w_cache * out_q[b, hq] + w_new * vn[b, hq // G]) / (w_cache + w_new)
+    return out
+
+
 def window_quantized(length: int, sink: int, keep: int, flush: int) -> int:
     """Full-precision windows ([W] §4.4): positions quantized once a sequence has grown to
     `length` and every waiting batch of `flush` eligible positions has been quantized.

@@ -114,3 +114,53 @@ def test_values_do_not_move_probabilities(orc):
     e7[7] = 1
     assert np.allclose(out2, e7, atol=1e-12)       # probabilities sum to one
     assert not np.allclose(out1, out2)
+
+
+@pytest.mark.parametrize("t", [False, True])
+def test_decode_step_matches_torch_sdpa_fp64(orc, t):
+    """The step's attention: positions [0, L-1) from the cache, the new token from its own
+    full-precision row; torch fp64 attention over the dequantized cache rows followed by the
+    new row (with a key transform, the new key k_new T against q T^-T)."""
+    bits = (2, 4)
+    lens = (130, 64, 1, 0)
+    kp, vp, bt, seq, _, q, tinv = _setup(orc, B=4, seq_lens=lens, bits=bits, t=t, seed=3)
+    rng = np.random.default_rng(9)
+    Hq, Hkv = q.shape[1], kp.shape[1]
+    kn = rng.standard_normal((4, Hkv, 128)).astype(np.float32) * 1.5
+    vn = rng.standard_normal((4, Hkv, 128)).astype(np.float32)
+    got = orc.decode_step(kp, vp, q, bt, seq, kn, vn, t_inv_t=tinv, bits_k=bits[0], bits_v=bits[1])
+    ref = np.zeros_like(got)
+    for b, n in enumerate(lens):
+        if n == 0:
+            continue
+        sl = synth.slots_for(bt[b:b + 1], [n - 1])
+        kd = torch.tensor(orc.dequant(kp, 0, bits[0], sl), dtype=torch.float64)    # [n-1,Hkv,d]
+        vd = torch.tensor(orc.dequant(vp, 1, bits[1], sl), dtype=torch.float64)
+        knb = torch.tensor(kn[b], dtype=torch.float64)                             # [Hkv,d]
+        qb = torch.tensor(q[b], dtype=torch.float64)
+        if tinv is not None:
+            tin = torch.tensor(tinv, dtype=torch.float64)
+            tk = torch.linalg.inv(tin.transpose(1, 2))                             # T = (T^-T)^-T
+            knb = torch.stack([knb[h] @ tk[h] for h in range(Hkv)])
+            qb = torch.stack([qb[h] @ tin[h // (Hq // Hkv)] for h in range(Hq)])
+        kk = torch.cat([kd, knb[None]], 0).permute(1, 0, 2).repeat_interleave(Hq // Hkv, dim=0)
+        vv = torch.cat([vd, torch.tensor(vn[b], dtype=torch.float64)[None]], 0).permute(1, 0, 2)
+        vv = vv.repeat_interleave(Hq // Hkv, dim=0)
+        o = torch.nn.functional.scaled_dot_product_attention(qb[:, None, :], kk, vv)
+        ref[b] = o[:, 0, :].numpy()
+    assert np.all(got[3] == 0)                                       # no tokens, no output
+    assert np.allclose(got[2], np.repeat(vn[2], Hq // Hkv, axis=0), rtol=0, atol=1e-12)   # only the new token
+    assert np.max(np.abs(got - ref)) < 1e-10 * max(1.0, np.max(np.abs(ref)))
+
+
+def test_decode_step_equals_decode_when_the_new_row_is_the_cached_one(orc):
+    """If the new token's row is exactly what the cache holds at position L-1 (no key
+    transform), the step is the plain decode over [0, L)."""
+    bits = (3, 2)
+    kp, vp, bt, seq, _, q, _ = _setup(orc, B=3, seq_lens=(130, 64, 1), bits=bits, t=False, seed=5)
+    last = np.array([synth.slots_for(bt[b:b + 1], [int(n)])[-1] for b, n in enumerate(seq)], np.int64)
+    kn = orc.dequant(kp, 0, bits[0], last)
+    vn = orc.dequant(vp, 1, bits[1], last)
+    got = orc.decode_step(kp, vp, q, bt, seq, kn, vn, bits_k=bits[0], bits_v=bits[1])
+    ref = orc.decode_attention(kp, vp, q, bt, seq, bits_k=bits[0], bits_v=bits[1])
+    assert np.max(np.abs(got - ref)) < 1e-12 * max(1.0, np.max(np.abs(ref)))
