@@ -107,8 +107,8 @@ def decode_workspace_bytes(cache: KVCache, batch: int, num_q_heads: int, max_seq
 
 
 def decode_step_workspace_bytes(cache: KVCache, batch: int, num_q_heads: int, max_seq_len: int) -> int:
-    """Workspace bytes with which kvq_decode_step builds the decode's query operands beside
-    its append (batches of up to 512 sequences); decode_workspace_bytes is the minimum."""
+    """Workspace bytes with which kvq_decode_step builds the decode's query operands once,
+    before its decode (batches of up to 512 sequences); decode_workspace_bytes is the minimum."""
     d = cache.desc()
     return int(load().kvq_decode_step_workspace_bytes(C.byref(d), batch, num_q_heads, max_seq_len))
 
@@ -176,8 +176,10 @@ def kvq_decode_step(cache: KVCache, q: torch.Tensor, k_new: torch.Tensor, v_new:
                     t_k_inv_t: torch.Tensor | None = None, sm_scale: float | None = None,
                     out: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
                     stream=None) -> torch.Tensor:
-    """Append each sequence's new token (k_new, v_new: [B, kv_heads, 128]; new_slots: [B]
-    int64, the slot of position seq_lens[b]-1) and decode, in one launch.  Returns out."""
+    """One decode step: each sequence's new token (k_new, v_new: [B, kv_heads, 128]; position
+    seq_lens[b]-1) takes part in the attention at full precision beside positions
+    [0, seq_lens[b]-1) of the cache, and is quantized into the cache at new_slots[b] ([B]
+    int64) for later steps.  Returns out."""
     B, Hq = _read_shapes(cache, q, block_table, seq_lens, t_k_inv_t, out)
     H = cache.num_kv_heads
     _shape(k_new, "k_new", B, H, HEAD_DIM); _shape(v_new, "v_new", B, H, HEAD_DIM)

@@ -295,18 +295,23 @@ kvq_status kvq_decode_step(const kvq_cache_desc* cache, const void* q, const voi
   if (t_k && t_dtype != dtype) return fail(KVQ_ERR_UNSUPPORTED, "t_dtype must equal dtype");
   if (batch == 0) return KVQ_OK;
   if (!k_new || !v_new || !new_slots) return fail(KVQ_ERR_INVALID_ARG, "k_new, v_new and new_slots must be non-null");
-  // two launches in stream order: the append, then the decode that reads it.  (Writing the
-  // new token inside the decode kernel, by the workgroup that reads the last page, measured
-  // slower: its latency lands at the start of every workgroup, before the page stream.)
-  // The query operands need no cache, so when the decode splits sequences over several
-  // workgroups (each of which would build the same operands) and the workspace has room
-  // for them, the append launch builds them once.  Without a split the decode builds them
-  // while its first pages load, which measured no slower than reading them.
+  // The new token of each sequence takes part in the attention from k_new / v_new at full
+  // precision (the decode reads positions [0, seq_len - 1) from the cache), and its codes
+  // are written for later steps by an append that the decode does not wait for: the decode
+  // masks position seq_len - 1 out of the last page it loads.
+  //  * Without a split, the append runs in the decode's own launch, in blocks after the
+  //    decode's: dispatched last, they take the slots that the first decode workgroups leave
+  //    while the last ones still walk their pages.
+  //  * When the decode splits sequences over several workgroups (each of which would build
+  //    the same query operands) and the workspace has room for them, a first launch appends
+  //    and builds the operands once; the decode reads them.
+  //  * Otherwise the append is a launch of its own before the decode.
   const kvq::AppendParams a = append_params(cache, k_new, v_new, new_slots, batch, t_k);
   const hipStream_t st = static_cast<hipStream_t>(stream);
+  p.knew = k_new;
+  p.vnew = v_new;
   if (p.chunks > 1 && batch <= kvq::kStepPrepMaxTokens &&
       workspace_bytes >= kvq_decode_step_workspace_bytes(cache, batch, num_q_heads, max_seq_len)) {
-    // the append launch also builds the query operands, which the decode then reads
     kvq::StepPrepParams sp;
     sp.a = a;
     sp.d = p;
@@ -315,9 +320,12 @@ kvq_status kvq_decode_step(const kvq_cache_desc* cache, const void* q, const voi
     sp.n_tokens = batch;
     if ((s = hip_status(kvq::launch_step_prep(sp, (int)dtype, cache->bits_k, st))) != KVQ_OK) return s;
     p.qop = sp.qop;
-    return hip_status(kvq::launch_decode(p, cache->bits_k, cache->bits_v, (int)dtype, st));
+  } else if (p.chunks == 1 && batch <= 32767) {
+    p.app = a;
+    p.append_blocks = 1;
+  } else if ((s = hip_status(kvq::launch_append(a, (int)dtype, st))) != KVQ_OK) {
+    return s;
   }
-  if ((s = hip_status(kvq::launch_append(a, (int)dtype, st))) != KVQ_OK) return s;
   return hip_status(kvq::launch_decode(p, cache->bits_k, cache->bits_v, (int)dtype, st));
 }
 

@@ -432,6 +432,16 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
   constexpr int BVL = low_bits<BV>();   // low-plane width of the values
   const int chunk = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  if (b >= p.batch) {
+    // a decode step's append, in the blocks after the decode's: dispatched last, they run in
+    // the slots that the first decode workgroups leave while the last ones still walk
+    __shared__ float app_part[4][kHeadDim];
+    if (p.append_blocks && chunk == 0) {
+      if (select_width(p.app) == 3) append_token<TQ, 3, 1>(p.app, b - p.batch, kvh, wave, lane, app_part);
+      else append_token<TQ, 0, 1>(p.app, b - p.batch, kvh, wave, lane, app_part);
+    }
+    return;
+  }
   const int kg = lane >> 4, n = lane & 15;
   const int beta = n / GP;           // column block of this lane
   const int G = p.group;
@@ -442,8 +452,10 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
 
   // ---- this wave's pages ----
   // with full-precision windows the cache holds the quantized middle positions only
+  // a decode step's new token (position seq_len - 1) comes from the step's rows, not the cache
+  const bool new_tok = p.knew != nullptr && p.seq_lens[b] > 0;
   const int nseq = min(p.win.flush > 0 ? window_quantized(max(p.seq_lens[b] - p.win_pending, 0), p.win)
-                                       : p.seq_lens[b],
+                                       : p.seq_lens[b] - (new_tok ? 1 : 0),
                        p.max_pages * kPageTokens);
   const int npages = (nseq + kPageTokens - 1) / kPageTokens;
   const int wv = chunk * kWaves + wave;
@@ -485,8 +497,8 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
 
   // ---- prologue: the query operands ----
   // Computed here (q and T^-T loads first, then the first pages' loads, so the arithmetic
-  // overlaps the page fetch), or, in a decode step, read from the image that the step's
-  // append launch built.
+  // overlaps the page fetch), or, in a split decode step, read from the image that the
+  // step's operand launch built.
   const bool pre = p.qop != nullptr;
   QLoads<TQ, GP> L;
   if (!pre) q_issue_loads<TQ, GP>(p, b, kvh, wave, lane, L);
@@ -866,6 +878,22 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
     red_ml[wave][n][0] = mlog2;
     red_ml[wave][n][1] = any_page ? l : 0.0f;
   }
+  // the step's new token joins the merge of chunk 0 as one more part: its score q.k_new
+  // (log2 units; q'.k' = q.k, so no transform), weight 1 and value row v_new.  Wave w sums
+  // the products of heads w, w + 4, ... over its lanes' channel pairs.
+  __shared__ float s_new[16];
+  const bool new_part = new_tok && chunk == 0;
+  if (new_part) {
+    const TQ* krow = reinterpret_cast<const TQ*>(p.knew) + ((int64_t)b * p.heads_kv + kvh) * kHeadDim;
+    const float k0 = Elem<TQ>::get(krow, 2 * lane), k1 = Elem<TQ>::get(krow, 2 * lane + 1);
+    for (int gg = wave; gg < G; gg += kWaves) {
+      const TQ* qrow = reinterpret_cast<const TQ*>(p.q) + ((int64_t)b * p.heads_q + (int64_t)kvh * G + gg) * kHeadDim;
+      float d = __builtin_fmaf(Elem<TQ>::get(qrow, 2 * lane), k0, Elem<TQ>::get(qrow, 2 * lane + 1) * k1);
+#pragma unroll
+      for (int off = 32; off >= 1; off >>= 1) d += __shfl_xor(d, off);
+      if (lane == 0) s_new[gg] = d * p.score_scale;
+    }
+  }
   __syncthreads();
 
   // ---- merge the waves and the column blocks of each head ----
@@ -884,7 +912,12 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
         lw[w * NB + bb] = red_ml[w][col][1];
         ow[w * NB + bb] = red_o[w][col][ch];
       }
-    float M = -__builtin_inff();
+    // the new token's part (chunk 0 of a step: score, weight 1, value; else no part)
+    const float m_nt = new_part ? s_new[gg] : -__builtin_inff();
+    const float v_nt = new_part
+        ? Elem<TQ>::get(reinterpret_cast<const TQ*>(p.vnew) + ((int64_t)b * p.heads_kv + kvh) * kHeadDim, ch)
+        : 0.0f;
+    float M = m_nt;
 #pragma unroll
     for (int k = 0; k < NP; ++k) M = fmaxf(M, mw[k]);
     // a part without tokens (m = -inf) is left out by a select: its other fields are not
@@ -898,6 +931,11 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
       const float f = __builtin_amdgcn_exp2f(mw[k] - Mf);
       L = live ? __builtin_fmaf(lw[k], f, L) : L;
       O = live ? __builtin_fmaf(ow[k], f, O) : O;
+    }
+    if (new_part) {
+      const float f = __builtin_amdgcn_exp2f(m_nt - Mf);
+      L += f;
+      O = __builtin_fmaf(v_nt, f, O);
     }
     const int hq = hq0 + gg;
     if (p.chunks == 1 && p.win.flush == 0) {
@@ -966,7 +1004,7 @@ __global__ __launch_bounds__(128) void combine_kernel(DecodeParams p) {
 
 template <typename TQ, int BK, int BV>
 hipError_t launch_typed(const DecodeParams& p, hipStream_t stream) {
-  const dim3 grid((unsigned)p.chunks, (unsigned)p.heads_kv, (unsigned)p.batch);
+  const dim3 grid((unsigned)p.chunks, (unsigned)p.heads_kv, (unsigned)(p.append_blocks ? 2 * p.batch : p.batch));
   switch (p.gpad) {
     case 4: hipLaunchKernelGGL((decode_kernel<TQ, BK, BV, 4>), grid, dim3(kThreads), 0, stream, p); break;
     case 8: hipLaunchKernelGGL((decode_kernel<TQ, BK, BV, 8>), grid, dim3(kThreads), 0, stream, p); break;
@@ -987,11 +1025,10 @@ hipError_t launch_bits(const DecodeParams& p, int q_dtype, hipStream_t stream) {
   }
 }
 
-// A decode step's first launch.  Workgroups x < n_tokens append token x for KV head y (the
-// small append path's work, with 4 waves: wave 1 writes the value); the others build the
+// A split decode step's first launch.  Workgroups x < n_tokens append token x for KV head y
+// (the small append path's work, with 4 waves: wave 1 writes the value); the others build the
 // query operands of (sequence x - n_tokens, KV head y) with the decode kernel's own code and
-// store them in the image.  The operands do not depend on the cache, so they are built while
-// the append runs instead of at the start of every decode workgroup.
+// store them in the image, once instead of at the start of every decode workgroup.
 template <typename TIn, int KSEL, int BK, int GP>
 __global__ __launch_bounds__(kThreads) void step_prep_kernel(StepPrepParams sp) {
   constexpr int kLdsFloats = GP * kQRow > 4 * kHeadDim ? GP * kQRow : 4 * kHeadDim;

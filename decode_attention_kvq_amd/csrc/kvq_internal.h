@@ -97,9 +97,19 @@ struct DecodeParams {
   // always go to the workspace, and the window kernel merges them
   WindowShape win;
   int win_pending;
-  // a decode step's query operands, built beside the step's append (null: the decode kernel
+  // a decode step's query operands, built by a launch before the decode (null: the decode kernel
   // builds them itself); qop_dwords(gpad) words per (sequence, KV head)
   const uint32_t* qop;
+  // a decode step's new tokens, [B][Hkv][128] of the query's type (null: none): position
+  // seq_len - 1 of each non-empty sequence takes part from these rows at full precision, and
+  // the cache supplies positions [0, seq_len - 1)
+  const void* knew;
+  const void* vnew;
+  // a decode step without a split: append_blocks = 1 adds batch z-blocks to the grid, and
+  // block (0, h, batch + i) appends token i of `app` for KV head h (this launch never reads
+  // what they write: the new tokens take part from knew / vnew)
+  int append_blocks;
+  AppendParams app;
 };
 
 // Words of the query-operand image of one (sequence, KV head) at gp query heads per KV head:

@@ -126,7 +126,7 @@ kvq_status kvq_quantize_append(const kvq_cache_desc* cache, const void* k, const
 size_t kvq_decode_workspace_bytes(const kvq_cache_desc* cache, int32_t batch,
                                   int32_t num_q_heads, int32_t max_seq_len);
 
-/* Workspace bytes with which kvq_decode_step builds the query operands beside its append.
+/* Workspace bytes with which kvq_decode_step builds the query operands once, before its decode.
  * When the decode splits each sequence over several workgroups and batch <= 512:
  * kvq_decode_workspace_bytes() plus an image of 400 bytes per query head, rounded up to
  * 4, 8 or 16 per KV head, for every (sequence, KV head), with the same partial-output
@@ -178,28 +178,36 @@ kvq_status kvq_decode_attn_noalloc(const kvq_cache_desc* cache, const void* q, k
                                    const int32_t* seq_lens, int32_t max_seq_len, float sm_scale,
                                    float* out, void* stream);
 
-/* One decode step with the step's new tokens: for every sequence b, the key and value of
- * its new token (all KV heads) are encoded exactly as kvq_quantize_append encodes them and
- * written at new_slots[b]; then sequence b is read as by kvq_decode_attn over positions
- * [0, seq_lens[b]), the new token included.  This is the write path of "WUSH-KV: KV Cache
- * Quantization with Data-Adaptive Transforms" §4.2/§4.3 followed by its read path (§4.1,
- * §4.2) as one call (two kernels in stream order on `stream`).
+/* One decode step with the step's new tokens, in the order "WUSH-KV: KV Cache Quantization
+ * with Data-Adaptive Transforms" §4.4 gives a new entry: it first takes part in attention
+ * at full precision, and is quantized into the cache afterwards.  For every sequence b with
+ * seq_lens[b] > 0, position seq_lens[b]-1 is the new token: sequence b is read as by
+ * kvq_decode_attn over positions [0, seq_lens[b]-1) of the cache plus the new token's own
+ * key and value (k_new, v_new, unquantized; its score is q . k_new, which equals
+ * q' . k' under the key transform); and the new token's key and value (all KV heads) are
+ * encoded exactly as kvq_quantize_append encodes them and written at new_slots[b], for
+ * later steps.  The write path is [W] §4.2/§4.3, the read path §4.1/§4.2.  The decode does
+ * not wait for the append (it gives position seq_lens[b]-1 of the cache no weight): without
+ * a split of the sequences, the append runs in the decode's own launch, in workgroups after
+ * the decode's; with a split, in the launch that builds the query operands before it.  All
+ * launches are on `stream`.
  *   q, k_new, v_new  device, [batch][num_q_heads][128] and [batch][num_kv_heads][128] of
  *                 dtype (post-RoPE query and key; the value in the folded basis).
  *   new_slots     device, [batch] int64: the slot of position seq_lens[b]-1 of sequence b
  *                 (page block_table[b][(seq_lens[b]-1)/64], offset (seq_lens[b]-1)%64);
- *                 < 0 or >= num_pages*64: no new token for that sequence.  Another slot
- *                 is written, but the output may then miss it.
+ *                 < 0 or >= num_pages*64: nothing is written for that sequence (it still
+ *                 attends to its new token).  The slot must not be one that any sequence
+ *                 reads in this call (positions [0, seq_lens-1) of the block tables): the
+ *                 append may run while the decode reads.
  *   t_k           as in kvq_quantize_append (t_dtype must equal dtype); t_k_inv_t,
  *                 block_table, seq_lens, max_seq_len, sm_scale, out as in kvq_decode_attn.
  *   workspace     device scratch, owned by the caller, of at least
  *                 kvq_decode_workspace_bytes() bytes (KVQ_ERR_WORKSPACE otherwise).  With
  *                 kvq_decode_step_workspace_bytes() bytes, when the decode splits each
- *                 sequence over several workgroups and batch <= 512, the first launch also
- *                 builds the decode's query operands (q' = q . T_K^-T as fp6 terms) for
- *                 every (sequence, KV head) while it appends, and the decode reads them
- *                 instead of building them in every workgroup; the output is the same bit
- *                 for bit.
+ *                 sequence over several workgroups and batch <= 512, a launch before the
+ *                 decode builds its query operands (q' = q . T_K^-T as fp6 terms) once for
+ *                 every (sequence, KV head), and the decode reads them instead of building
+ *                 them in every workgroup; the output is the same bit for bit.
  * The written bytes equal those of kvq_quantize_append for the same new tokens. */
 kvq_status kvq_decode_step(const kvq_cache_desc* cache, const void* q, const void* k_new,
                            const void* v_new, kvq_dtype dtype, int32_t batch,

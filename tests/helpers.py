@@ -112,6 +112,26 @@ def oracle_decode_sequence(k_pool, v_pool, q, pages, seq_len, t_inv_t=None, **kw
         return np.concatenate(list(ex.map(head, range(H))), axis=0)
 
 
+def oracle_step_sequence(k_pool, v_pool, q, pages, seq_len, k_new, v_new, t_inv_t=None, **kw):
+    """oracle.decode_step of one sequence (q [Hq, 128], its pages in order, its new token's
+    rows k_new, v_new [H, 128]), one KV head per worker thread; returns [Hq, 128] fp64."""
+    from concurrent.futures import ThreadPoolExecutor
+    H = k_pool.shape[1]
+    G = q.shape[0] // H
+    kp = k_pool[pages]
+    vp = v_pool[pages]
+    bt = np.arange(len(pages), dtype=np.int32)[None]
+    seq = np.array([seq_len], np.int32)
+
+    def head(h):
+        ti = None if t_inv_t is None else t_inv_t[h:h + 1]
+        return oracle.decode_step(np.ascontiguousarray(kp[:, h:h + 1]), np.ascontiguousarray(vp[:, h:h + 1]),
+                                  q[None, h * G:(h + 1) * G], bt, seq, k_new[None, h:h + 1], v_new[None, h:h + 1],
+                                  t_inv_t=ti, **kw)[0]
+    with ThreadPoolExecutor(_threads(H)) as ex:
+        return np.concatenate(list(ex.map(head, range(H))), axis=0)
+
+
 def pool_scales_zeros(pool: np.ndarray, bits: int, slots):
     """fp16 bit patterns of the scale and zero of every (slot, KV head): [n, H] each, read
     straight from the block layout (64 scales, then 64 zeros, after the code section)."""

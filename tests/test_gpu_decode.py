@@ -238,9 +238,9 @@ def test_qwen3_8b_b1_16k_full():
                                     bits_k=2, bits_v=2)
     assert row_rel_err(got, ref_g).max() <= TOL
     assert row_rel_err(got, ref).max() <= TOL
-    # a decode step as the benchmark runs it: the new token rewrites the last position, and
-    # with the step's full workspace the append launch also builds the query operands that
-    # the 16 chunks read
+    # a decode step as the benchmark runs it: the new token rewrites the last position and
+    # takes part at full precision, and with the step's full workspace a launch before the
+    # decode builds the query operands that the 16 chunks read
     rng_new = np.random.default_rng(12)
     kn = rng_new.standard_normal((1, H, 128)).astype(np.float32)
     vn = rng_new.standard_normal((1, H, 128)).astype(np.float32)
@@ -258,8 +258,10 @@ def test_qwen3_8b_b1_16k_full():
     oracle.append(kp, vp, kn.float().numpy(), vn.float().numpy(), new_slot, t_k=t, bits_k=2, bits_v=2)
     gv = cache.v_pages.cpu().numpy()
     assert np.array_equal(gv, vp)
-    ref = oracle.decode_attention(kp, vp, q, bt, seq, t_inv_t=tinv, bits_k=2, bits_v=2)
-    ref_g = oracle.decode_attention(cache.k_pages.cpu().numpy(), gv, q, bt, seq, t_inv_t=tinv, bits_k=2, bits_v=2)
+    knf, vnf = kn.float().numpy(), vn.float().numpy()
+    ref = oracle.decode_step(kp, vp, q, bt, seq, knf, vnf, t_inv_t=tinv, bits_k=2, bits_v=2)
+    ref_g = oracle.decode_step(cache.k_pages.cpu().numpy(), gv, q, bt, seq, knf, vnf, t_inv_t=tinv, bits_k=2,
+                               bits_v=2)
     assert row_rel_err(got, ref_g).max() <= TOL
     assert row_rel_err(got, ref).max() <= TOL
 

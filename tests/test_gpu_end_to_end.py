@@ -10,11 +10,11 @@ decode, and:
   * the GPU output matches the oracle's decode of the GPU-written pages, and the oracle's
     write + decode, within 2e-3 per (sequence, query head) row.
 Then one decode step (kvq_decode_step) in the benchmark's configuration: a new token
-rewrites every sequence's last position, with the step's full workspace (the long-context
-workload splits its sequences, so the step's append launch also builds the decode's query
-operands).  The sampled sequences' value pages equal the oracle's append of the same token
-into its pages bit for bit, and the output is within 2e-3 of the oracle's decode of the
-GPU's pages and of its own pages.
+rewrites every sequence's last position and takes part at full precision, with the step's
+full workspace (the long-context workload splits its sequences, so a launch before the
+decode builds its query operands).  The sampled sequences' value pages equal the oracle's
+append of the same token into its pages bit for bit, and the output is within 2e-3 of the
+oracle's step over the GPU's pages and over its own pages.
 Write path: "WUSH-KV: KV Cache Quantization with Data-Adaptive Transforms" §4.2, §4.3
 (QuEST, alpha = 2.83, on the long-context workload) and §5.3 (percentile 1%/99%); read
 path: §4.1, §4.2; long contexts as in its App. D.3.
@@ -25,8 +25,8 @@ import torch
 
 import oracle
 from decode_attention_kvq_amd import api, calib, synth
-from helpers import (f16_ulp_distance, oracle_append_sequence, oracle_decode_sequence, pool_codes,
-                     pool_scales_zeros, row_rel_err, SCALE_ZERO_RATE)
+from helpers import (f16_ulp_distance, oracle_append_sequence, oracle_decode_sequence, oracle_step_sequence,
+                     pool_codes, pool_scales_zeros, row_rel_err, SCALE_ZERO_RATE)
 
 pytestmark = pytest.mark.gpu
 
@@ -123,8 +123,10 @@ def test_full_size_end_to_end(name, samples):
                       alpha_v=w.alpha)
         assert np.array_equal(gv, vp), b
         all_pages = np.arange(pps)
-        ref_g = oracle_decode_sequence(gk, gv, q[b], all_pages, n, t_inv_t=tinv, bits_k=w.bits_k, bits_v=w.bits_v)
-        ref = oracle_decode_sequence(kp, vp, q[b], all_pages, n, t_inv_t=tinv, bits_k=w.bits_k, bits_v=w.bits_v)
+        ref_g = oracle_step_sequence(gk, gv, q[b], all_pages, n, kn[b], vn[b], t_inv_t=tinv, bits_k=w.bits_k,
+                                     bits_v=w.bits_v)
+        ref = oracle_step_sequence(kp, vp, q[b], all_pages, n, kn[b], vn[b], t_inv_t=tinv, bits_k=w.bits_k,
+                                   bits_v=w.bits_v)
         e_g = row_rel_err(got[b], ref_g).max()
         e = row_rel_err(got[b], ref).max()
         print(f"  step, sequence {b}: row-relative error vs oracle on GPU pages {e_g:.2e}, end to end {e:.2e}",

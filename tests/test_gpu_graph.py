@@ -104,7 +104,7 @@ def test_graph_replays_of_the_step_with_query_operand_image():
     the new tokens and writes the query-operand image into the workspace, and the decode and
     merge launches read it.  Captured once and replayed with the workspace scribbled over in
     between, every replay equals the eager step bit for bit, and the eager step matches the
-    oracle."""
+    oracle's step."""
     d = _setup([200, 2900, 64, 1])
     dev = torch.device("cuda")
     H = d["H"]
@@ -153,6 +153,7 @@ def test_graph_replays_of_the_step_with_query_operand_image():
     kp, vp = d["kp"].copy(), d["vp"].copy()
     oracle.append(kp, vp, d["k_new"], d["v_new"], d["new_slots"], t_k=d["t_k"].astype(np.float32),
                   bits_k=2, bits_v=2)
-    ref = oracle.decode_attention(kp, vp, d["q"], d["bt"], d["seq"], t_inv_t=d["t_inv"], bits_k=2, bits_v=2)
+    ref = oracle.decode_step(kp, vp, d["q"], d["bt"], d["seq"], d["k_new"], d["v_new"], t_inv_t=d["t_inv"],
+                             bits_k=2, bits_v=2)
     err = row_rel_err(eager_out.cpu().numpy(), ref)
     assert err.max() <= 2e-3, err.max()

@@ -3,10 +3,11 @@
 workgroups, where the step's first launch also builds the decode's query operands), 1 to 4
 KV heads, group sizes 1 to 16, every bit-width pair, both quantizers, the three input types,
 with and without a key transform, shuffled pages.  The oracle writes every position but the
-last, and the step appends the last one (a new token per sequence) and decodes.
+last; the step attends to the last one (a new token per sequence) at full precision and
+appends it.
   * values, and keys without a transform, are written exactly as the oracle appends them;
-  * the output is within 2e-3 per row of the oracle's append + decode, and equal bit for
-    bit to the step with only the decode's workspace (operands built in every workgroup)."""
+  * the output is within 2e-3 per row of the oracle's step, and equal bit for bit to the
+    step with only the decode's workspace (operands built in every workgroup)."""
 import zlib
 
 import numpy as np
@@ -54,13 +55,13 @@ def test_random_step_configuration(seed):
     assert np.array_equal(vf, vp), (info, describe_mismatch(vf, vp))
     if not with_t:
         assert np.array_equal(kf, kp), (info, describe_mismatch(kf, kp))
-    ref = oracle.decode_attention(kp, vp, s["q"], s["bt"], np.array(lens, np.int32), t_inv_t=s["tinv"],
-                                  bits_k=bits[0], bits_v=bits[1])
+    ref = oracle.decode_step(kp, vp, s["q"], s["bt"], np.array(lens, np.int32), s["knew"], s["vnew"],
+                             t_inv_t=s["tinv"], bits_k=bits[0], bits_v=bits[1])
     empty = np.array(lens) == 0
     assert np.all(out[empty] == 0), info
     err = row_rel_err(out[~empty], ref[~empty])
     assert err.max() <= 2e-3, (info, float(err.max()))
-    # a split decode builds its operands beside the append; with the decode's workspace only,
+    # a split decode's operands are built once before it; with the decode's workspace only,
     # every workgroup builds them itself, with the same code
     cache = api.KVCache(s["P"], H, bits[0], bits[1], quant[0], quant[1])
     split = api.decode_step_workspace_bytes(cache, B, H * G, max(lens)) > \
