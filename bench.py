@@ -1,9 +1,9 @@
 """Benchmark of one decode step of the quantized-KV-cache hot path on one MI355X.
 
-A step is the whole hot path over one batch: the batch's new tokens (one per sequence) are
-transformed, clipped, quantized to 2-bit percentile codes and packed into the cache, and
-every sequence is decoded over its whole cache, new token included: one kvq_decode_step
-launch.  Default workload: the Qwen3-8B-shaped layer (32 query heads, 8 KV heads, head_dim
+A step is the whole hot path over one batch: every sequence is decoded over its cache, with
+its new token at full precision, and the batch's new tokens (one per sequence) are
+transformed, clipped, quantized to 2-bit percentile codes and packed into the cache for
+later steps: one kvq_decode_step call.  Default workload: the Qwen3-8B-shaped layer (32 query heads, 8 KV heads, head_dim
 128) at batch 64 x 16384 cached tokens, 2-bit K and V, synthetic Sigma-model data, caches
 resident in HBM.
 
@@ -111,8 +111,8 @@ def setup_decode(w, torch, api, calib, synth, dev):
 
 
 def time_steps(w, s, torch, api, steps, warmup, before=None):
-    """Times the step, kvq_decode_step (the batch's new tokens appended, then every sequence
-    decoded), as one HIP-graph replay of `steps` consecutive steps (captured from the
+    """Times the step, kvq_decode_step (every sequence decoded with its new token at full
+    precision, the new tokens appended in the same launch), as one HIP-graph replay of `steps` consecutive steps (captured from the
     library calls, which launch on torch's current stream), after one replay of a graph of
     `warmup` steps, so the host's per-call and per-replay cost does not pace the GPU.  HIP
     events on the launch stream bracket the timed replay.  The append and the decode kernel
