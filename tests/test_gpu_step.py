@@ -7,8 +7,9 @@ steps by an append running beside the decode.
   * The output matches the oracle's step (positions [0, L-1) from the cache, the new token
     from its own row) within 2e-3 of each row's largest magnitude.
 Covered: single and split launches (long sequences), ragged lengths, a new token that
-opens a page, sequences without a new token, 2- and 4-bit codes, both quantizers, bf16
-inputs with a dense transform and fp32 inputs.
+opens a page, sequences without a new token, new tokens without a slot (attended, not
+written), 2- and 4-bit codes, both quantizers, bf16 inputs with a dense transform and fp32
+inputs.
 """
 import numpy as np
 import pytest
@@ -152,3 +153,35 @@ def test_step_query_operands_built_once(case):
     assert np.array_equal(out_i, out_m), np.abs(out_i - out_m).max()
     ref = _oracle_step(s, lens, bits, ki, vi)
     assert row_rel_err(out_i, ref).max() <= 2e-3
+
+
+# A sequence with a new token but no slot (slot < 0): the step still attends to its new
+# token at full precision and writes nothing for it; the other sequences append as usual.
+NO_SLOT_CASES = [
+    (CASES[0], [1, 3]),           # one launch, the append in the decode's own launch
+    (CASES[4], [0, 3, 4]),        # one launch, 4-bit, a 1- and a 2-token sequence without a slot
+    (CASES[2], [1]),              # split over chunks: the operand launch appends
+    (CASES[3], [0]),              # split, the only sequence without a slot: nothing is written
+]
+
+
+@pytest.mark.parametrize("case", range(len(NO_SLOT_CASES)))
+def test_step_without_a_slot_attends_and_writes_nothing(case):
+    (B, H, G, lens, bits, quant, dtype, transform), drop = NO_SLOT_CASES[case]
+    rng = np.random.default_rng(300 + case)
+    s = _setup(rng, B, H, G, lens, bits, quant, dtype, transform)
+    s["new_slots"] = s["new_slots"].copy()
+    s["new_slots"][drop] = -1
+    out_f, kf, vf = _gpu(s, H, bits, quant, dtype, lens, fused=True)
+    _, ks, vs = _gpu(s, H, bits, quant, dtype, lens, fused=False)
+    assert np.array_equal(kf, ks), describe_mismatch(kf, ks)
+    assert np.array_equal(vf, vs), describe_mismatch(vf, vs)
+    kp, vp = s["kp"].copy(), s["vp"].copy()
+    oracle.append(kp, vp, s["knew"], s["vnew"], s["new_slots"], t_k=s["t"], **s["kw"])
+    # the pages of the sequences without a slot are the starting ones
+    for b in drop:
+        for pg in s["bt"][b, :-(-lens[b] // 64)]:
+            assert np.array_equal(vf[pg], s["vp"][pg]) and np.array_equal(kf[pg], s["kp"][pg])
+    ref = _oracle_step(s, lens, bits, kp, vp)
+    assert row_rel_err(out_f, ref).max() <= 2e-3
+    assert np.array_equal(vf, vp), describe_mismatch(vf, vp)
