@@ -107,8 +107,8 @@ def decode_workspace_bytes(cache: KVCache, batch: int, num_q_heads: int, max_seq
 
 
 def decode_step_workspace_bytes(cache: KVCache, batch: int, num_q_heads: int, max_seq_len: int) -> int:
-    """Workspace bytes with which kvq_decode_step builds the decode's query operands once,
-    before its decode (batches of up to 512 sequences); decode_workspace_bytes is the minimum."""
+    """Workspace bytes of kvq_decode_step: the same as decode_workspace_bytes (the step's
+    append runs in the decode's own launch and needs no workspace)."""
     d = cache.desc()
     return int(load().kvq_decode_step_workspace_bytes(C.byref(d), batch, num_q_heads, max_seq_len))
 

@@ -100,13 +100,6 @@ int split_length(int max_seq_len, const kvq::WindowShape* win) {
   return win ? (max_seq_len > win->sink ? max_seq_len - win->sink : 0) : max_seq_len;
 }
 
-// Byte offset of a decode step's query-operand image in its workspace: after the decode's
-// partial outputs, 256-byte aligned.
-size_t step_qop_offset(const kvq_cache_desc* cache, int32_t batch, int32_t num_q_heads, int32_t max_seq_len) {
-  const kvq::DecodeSplit sp = kvq::decode_split(batch, cache->num_kv_heads, max_seq_len);
-  return (workspace_layout(batch, num_q_heads, sp.chunks).total + 255) & ~(size_t)255;
-}
-
 // Checks and fills the decode launch; shared by the plain and windowed decodes.  With
 // windows (win non-null) the partial results always go to the workspace.
 kvq_status decode_params(const kvq_cache_desc* cache, const void* q, kvq_dtype q_dtype, int32_t batch,
@@ -223,14 +216,7 @@ size_t kvq_decode_workspace_bytes(const kvq_cache_desc* cache, int32_t batch, in
 
 size_t kvq_decode_step_workspace_bytes(const kvq_cache_desc* cache, int32_t batch, int32_t num_q_heads,
                                        int32_t max_seq_len) {
-  if (!cache || cache->num_kv_heads < 1 || batch <= 0 || num_q_heads < 1 || max_seq_len < 0 ||
-      num_q_heads % cache->num_kv_heads != 0 || num_q_heads / cache->num_kv_heads > 16)
-    return 0;
-  const kvq::DecodeSplit sp = kvq::decode_split(batch, cache->num_kv_heads, max_seq_len);
-  if (sp.chunks == 1 || batch > kvq::kStepPrepMaxTokens)   // no image: the decode's own workspace
-    return kvq_decode_workspace_bytes(cache, batch, num_q_heads, max_seq_len);
-  return step_qop_offset(cache, batch, num_q_heads, max_seq_len) +
-         (size_t)batch * cache->num_kv_heads * kvq::qop_dwords(kvq::decode_group_pad(num_q_heads / cache->num_kv_heads)) * 4;
+  return kvq_decode_workspace_bytes(cache, batch, num_q_heads, max_seq_len);
 }
 
 kvq_status kvq_decode_attn(const kvq_cache_desc* cache, const void* q, kvq_dtype q_dtype, int32_t batch,
@@ -298,29 +284,15 @@ kvq_status kvq_decode_step(const kvq_cache_desc* cache, const void* q, const voi
   // The new token of each sequence takes part in the attention from k_new / v_new at full
   // precision (the decode reads positions [0, seq_len - 1) from the cache), and its codes
   // are written for later steps by an append that the decode does not wait for: the decode
-  // masks position seq_len - 1 out of the last page it loads.
-  //  * Without a split, the append runs in the decode's own launch, in blocks after the
-  //    decode's: dispatched last, they take the slots that the first decode workgroups leave
-  //    while the last ones still walk their pages.
-  //  * When the decode splits sequences over several workgroups (each of which would build
-  //    the same query operands) and the workspace has room for them, a first launch appends
-  //    and builds the operands once; the decode reads them.
-  //  * Otherwise the append is a launch of its own before the decode.
+  // masks position seq_len - 1 out of the last page it loads.  The append runs in the
+  // decode's own launch, in blocks after the decode's: dispatched last, they take the slots
+  // that the first decode workgroups leave while the last ones still walk their pages.  (A
+  // batch too large for the grid appends in a launch of its own first.)
   const kvq::AppendParams a = append_params(cache, k_new, v_new, new_slots, batch, t_k);
   const hipStream_t st = static_cast<hipStream_t>(stream);
   p.knew = k_new;
   p.vnew = v_new;
-  if (p.chunks > 1 && batch <= kvq::kStepPrepMaxTokens &&
-      workspace_bytes >= kvq_decode_step_workspace_bytes(cache, batch, num_q_heads, max_seq_len)) {
-    kvq::StepPrepParams sp;
-    sp.a = a;
-    sp.d = p;
-    sp.qop = reinterpret_cast<uint32_t*>(static_cast<char*>(workspace) +
-                                         step_qop_offset(cache, batch, num_q_heads, max_seq_len));
-    sp.n_tokens = batch;
-    if ((s = hip_status(kvq::launch_step_prep(sp, (int)dtype, cache->bits_k, st))) != KVQ_OK) return s;
-    p.qop = sp.qop;
-  } else if (p.chunks == 1 && batch <= 32767) {
+  if (batch <= 32767) {
     p.app = a;
     p.append_blocks = 1;
   } else if ((s = hip_status(kvq::launch_append(a, (int)dtype, st))) != KVQ_OK) {

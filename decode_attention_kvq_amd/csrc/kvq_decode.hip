@@ -416,13 +416,6 @@ __device__ __forceinline__ void q_build(const DecodeParams& p, int wave, int lan
   o.qsf4 = gq < G ? col_sum(s4) / kF : 0.0f;
 }
 
-// The operands of (sequence b, KV head kvh) in a step's image: for each head gq < GP and
-// channel group kg the 6 x kQTerms code words (at 24 (4 gq + kg)), then per head (e1, qsf3,
-// qsf4, 0) at 96 GP + 4 gq.  Written by the lanes of wave 0 with n < GP (one per (gq, kg)).
-__device__ __forceinline__ const uint32_t* qop_base(const uint32_t* img, int b, int kvh, int heads_kv, int gp) {
-  return img + ((int64_t)b * heads_kv + kvh) * qop_dwords(gp);
-}
-
 template <typename TQ, int BK, int BV, int GP>
 __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
   constexpr int NB = 16 / GP;        // column blocks
@@ -496,12 +489,10 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
   };
 
   // ---- prologue: the query operands ----
-  // Computed here (q and T^-T loads first, then the first pages' loads, so the arithmetic
-  // overlaps the page fetch), or, in a split decode step, read from the image that the
-  // step's operand launch built.
-  const bool pre = p.qop != nullptr;
+  // q and T^-T loads first, then the first pages' loads, so that the arithmetic that builds
+  // the operands overlaps the page fetch
   QLoads<TQ, GP> L;
-  if (!pre) q_issue_loads<TQ, GP>(p, b, kvh, wave, lane, L);
+  q_issue_loads<TQ, GP>(p, b, kvh, wave, lane, L);
   my_page = (lane < np && my_page >= 0 && my_page < p.num_pages) ? my_page : -1;
   my_page2 = (lane + 64 < np && my_page2 >= 0 && my_page2 < p.num_pages) ? my_page2 : -1;
   PageRegs<BK, BV, A> ring[PIPE];
@@ -509,32 +500,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
   for (int d = 0; d < PIPE; ++d) load(ring[d], d);
   __shared__ __attribute__((aligned(16))) float qs[GP * kQRow];
   QOperands qo;
-  if (pre) {
-    // the image's words of this lane's (head, channel group), then the head's scale
-    // exponent and sums (loaded and used in this one block)
-    const int gq = n % GP;
-    const uint32_t* base = qop_base(p.qop, b, kvh, p.heads_kv, GP);
-    const u32x4* src = reinterpret_cast<const u32x4*>(base + 24 * (4 * gq + kg));
-    u32x4 qw[7];
-#pragma unroll
-    for (int i = 0; i < 6; ++i) qw[i] = src[i];
-    qw[6] = *reinterpret_cast<const u32x4*>(base + 96 * GP + 4 * gq);
-#pragma unroll
-    for (int k = 0; k < kQTerms; ++k) {
-#pragma unroll
-      for (int d = 0; d < 6; ++d) qo.bq6[k][d] = (int)qw[(6 * k + d) / 4][(6 * k + d) % 4];
-      qo.bq6[k][6] = 0;
-      qo.bq6[k][7] = 0;
-    }
-    // each vector element goes through a scalar first: __builtin_bit_cast of an element of
-    // an ext_vector_type lvalue reads element 0
-    const uint32_t w0 = qw[6][0], w1 = qw[6][1], w2 = qw[6][2];
-    qo.e1 = (int)w0;
-    qo.qsf3 = __builtin_bit_cast(float, w1);
-    qo.qsf4 = __builtin_bit_cast(float, w2);
-  } else {
-    q_build<TQ, BK, GP>(p, wave, lane, L, qs, qo);
-  }
+  q_build<TQ, BK, GP>(p, wave, lane, L, qs, qo);
   v8i bq6[kQTerms];
   int sreg[kQTerms];
   constexpr float F = kF;
@@ -1025,60 +991,6 @@ hipError_t launch_bits(const DecodeParams& p, int q_dtype, hipStream_t stream) {
   }
 }
 
-// A split decode step's first launch.  Workgroups x < n_tokens append token x for KV head y
-// (the small append path's work, with 4 waves: wave 1 writes the value); the others build the
-// query operands of (sequence x - n_tokens, KV head y) with the decode kernel's own code and
-// store them in the image, once instead of at the start of every decode workgroup.
-template <typename TIn, int KSEL, int BK, int GP>
-__global__ __launch_bounds__(kThreads) void step_prep_kernel(StepPrepParams sp) {
-  constexpr int kLdsFloats = GP * kQRow > 4 * kHeadDim ? GP * kQRow : 4 * kHeadDim;
-  __shared__ __attribute__((aligned(16))) float lds[kLdsFloats];
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
-  if ((int)blockIdx.x < sp.n_tokens) {
-    append_token<TIn, KSEL, 1>(sp.a, blockIdx.x, blockIdx.y, wave, lane, reinterpret_cast<float (*)[kHeadDim]>(lds));
-    return;
-  }
-  const int b = (int)blockIdx.x - sp.n_tokens, kvh = blockIdx.y;
-  QLoads<TIn, GP> L;
-  q_issue_loads<TIn, GP>(sp.d, b, kvh, wave, lane, L);
-  QOperands o;
-  q_build<TIn, BK, GP>(sp.d, wave, lane, L, lds, o);
-  const int kg = lane >> 4, n = lane & 15;
-  if (wave == 0 && n < GP) {
-    uint32_t* base = sp.qop + ((int64_t)b * sp.d.heads_kv + kvh) * qop_dwords(GP);
-    u32x4* dst = reinterpret_cast<u32x4*>(base + 24 * (4 * n + kg));
-#pragma unroll
-    for (int i = 0; i < 6; ++i) {
-      u32x4 w;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) w[j] = (uint32_t)o.bq6[(4 * i + j) / 6][(4 * i + j) % 6];
-      dst[i] = w;
-    }
-    if (kg == 0)
-      *reinterpret_cast<u32x4*>(base + 96 * GP + 4 * n) =
-          u32x4{(uint32_t)o.e1, __builtin_bit_cast(uint32_t, o.qsf3), __builtin_bit_cast(uint32_t, o.qsf4), 0u};
-  }
-}
-
-template <typename TIn, int KSEL, int BK>
-hipError_t launch_prep_gp(const StepPrepParams& sp, hipStream_t stream) {
-  const dim3 grid((unsigned)(sp.n_tokens + sp.d.batch), (unsigned)sp.d.heads_kv);
-  switch (sp.d.gpad) {
-    case 4: hipLaunchKernelGGL((step_prep_kernel<TIn, KSEL, BK, 4>), grid, dim3(kThreads), 0, stream, sp); break;
-    case 8: hipLaunchKernelGGL((step_prep_kernel<TIn, KSEL, BK, 8>), grid, dim3(kThreads), 0, stream, sp); break;
-    default: hipLaunchKernelGGL((step_prep_kernel<TIn, KSEL, BK, 16>), grid, dim3(kThreads), 0, stream, sp); break;
-  }
-  return hipGetLastError();
-}
-
-template <typename TIn>
-hipError_t launch_prep_typed(const StepPrepParams& sp, int bits_k, hipStream_t stream) {
-  // the small path's percentile networks; key channel order of 4-bit keys or of the others
-  const bool k3 = select_width(sp.a) == 3;
-  if (bits_k == 4) return k3 ? launch_prep_gp<TIn, 3, 4>(sp, stream) : launch_prep_gp<TIn, 0, 4>(sp, stream);
-  return k3 ? launch_prep_gp<TIn, 3, 2>(sp, stream) : launch_prep_gp<TIn, 0, 2>(sp, stream);
-}
-
 }  // namespace
 
 int decode_group_pad(int group) { return group <= 4 ? 4 : (group <= 8 ? 8 : 16); }
@@ -1138,14 +1050,6 @@ hipError_t launch_decode(const DecodeParams& p, int bits_k, int bits_v, int q_dt
     case 42: return launch_bits<4, 2>(p, q_dtype, stream);
     case 43: return launch_bits<4, 3>(p, q_dtype, stream);
     default: return launch_bits<4, 4>(p, q_dtype, stream);
-  }
-}
-
-hipError_t launch_step_prep(const StepPrepParams& sp, int dtype, int bits_k, hipStream_t stream) {
-  switch (dtype) {
-    case 0: return launch_prep_typed<float>(sp, bits_k, stream);
-    case 1: return launch_prep_typed<__bf16>(sp, bits_k, stream);
-    default: return launch_prep_typed<_Float16>(sp, bits_k, stream);
   }
 }
 

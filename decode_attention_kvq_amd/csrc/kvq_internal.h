@@ -97,24 +97,18 @@ struct DecodeParams {
   // always go to the workspace, and the window kernel merges them
   WindowShape win;
   int win_pending;
-  // a decode step's query operands, built by a launch before the decode (null: the decode kernel
-  // builds them itself); qop_dwords(gpad) words per (sequence, KV head)
-  const uint32_t* qop;
   // a decode step's new tokens, [B][Hkv][128] of the query's type (null: none): position
   // seq_len - 1 of each non-empty sequence takes part from these rows at full precision, and
   // the cache supplies positions [0, seq_len - 1)
   const void* knew;
   const void* vnew;
-  // a decode step without a split: append_blocks = 1 adds batch z-blocks to the grid, and
-  // block (0, h, batch + i) appends token i of `app` for KV head h (this launch never reads
-  // what they write: the new tokens take part from knew / vnew)
+  // a decode step: append_blocks = 1 adds batch z-blocks to the grid, and block
+  // (0, h, batch + i) appends token i of `app` for KV head h (blocks (c > 0, h, batch + i)
+  // of a split decode do nothing); this launch never reads what they write: the new tokens
+  // take part from knew / vnew
   int append_blocks;
   AppendParams app;
 };
-
-// Words of the query-operand image of one (sequence, KV head) at gp query heads per KV head:
-// per head, 24 code words for each of the 4 channel groups and 4 words (e1, sums, pad).
-constexpr int qop_dwords(int gp) { return gp * 100; }
 
 // The window half of a windowed decode: attention over the full-precision positions, the
 // merge with the quantized partials, and (decode step) the store of the new token.
@@ -160,18 +154,7 @@ hipError_t launch_dequant(const DequantParams& p, hipStream_t stream);
 hipError_t launch_window(const DecodeParams& p, const WindowParams& w, int q_dtype, hipStream_t stream);
 hipError_t launch_window_store(const WindowStoreParams& p, int dtype, hipStream_t stream);
 
-// A decode step's first launch: the append of its n_tokens new tokens (the small append
-// path, so n_tokens <= kStepPrepMaxTokens) and, in the same grid, the query-operand image
-// (qop, qop_dwords(d.gpad) words per (sequence, KV head)) that the step's decode then reads.
 constexpr int kSmallAppendMaxTokens = 512;    // batches of up to this many tokens take the small path
-constexpr int kStepPrepMaxTokens = kSmallAppendMaxTokens;
-struct StepPrepParams {
-  AppendParams a;
-  DecodeParams d;
-  uint32_t* qop;
-  int n_tokens;
-};
-hipError_t launch_step_prep(const StepPrepParams& sp, int dtype, int bits_k, hipStream_t stream);
 
 // Split of a decode launch, a function of the shapes only.
 struct DecodeSplit {

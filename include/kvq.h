@@ -126,12 +126,8 @@ kvq_status kvq_quantize_append(const kvq_cache_desc* cache, const void* k, const
 size_t kvq_decode_workspace_bytes(const kvq_cache_desc* cache, int32_t batch,
                                   int32_t num_q_heads, int32_t max_seq_len);
 
-/* Workspace bytes with which kvq_decode_step builds the query operands once, before its decode.
- * When the decode splits each sequence over several workgroups and batch <= 512:
- * kvq_decode_workspace_bytes() plus an image of 400 bytes per query head, rounded up to
- * 4, 8 or 16 per KV head, for every (sequence, KV head), with the same partial-output
- * region as kvq_decode_attn first.  Otherwise the step builds no image and this equals
- * kvq_decode_workspace_bytes().  0 for invalid arguments. */
+/* Workspace bytes of kvq_decode_step: the step needs no more than its decode, so this equals
+ * kvq_decode_workspace_bytes() (0 for invalid arguments). */
 size_t kvq_decode_step_workspace_bytes(const kvq_cache_desc* cache, int32_t batch,
                                        int32_t num_q_heads, int32_t max_seq_len);
 
@@ -187,10 +183,9 @@ kvq_status kvq_decode_attn_noalloc(const kvq_cache_desc* cache, const void* q, k
  * q' . k' under the key transform); and the new token's key and value (all KV heads) are
  * encoded exactly as kvq_quantize_append encodes them and written at new_slots[b], for
  * later steps.  The write path is [W] §4.2/§4.3, the read path §4.1/§4.2.  The decode does
- * not wait for the append (it gives position seq_lens[b]-1 of the cache no weight): without
- * a split of the sequences, the append runs in the decode's own launch, in workgroups after
- * the decode's; with a split, in the launch that builds the query operands before it.  All
- * launches are on `stream`.
+ * not wait for the append (it gives position seq_lens[b]-1 of the cache no weight): the
+ * append runs in the decode's own launch, in workgroups after the decode's (a batch above
+ * 32767 appends in a launch of its own first).  All launches are on `stream`.
  *   q, k_new, v_new  device, [batch][num_q_heads][128] and [batch][num_kv_heads][128] of
  *                 dtype (post-RoPE query and key; the value in the folded basis).
  *   new_slots     device, [batch] int64: the slot of position seq_lens[b]-1 of sequence b
@@ -202,12 +197,7 @@ kvq_status kvq_decode_attn_noalloc(const kvq_cache_desc* cache, const void* q, k
  *   t_k           as in kvq_quantize_append (t_dtype must equal dtype); t_k_inv_t,
  *                 block_table, seq_lens, max_seq_len, sm_scale, out as in kvq_decode_attn.
  *   workspace     device scratch, owned by the caller, of at least
- *                 kvq_decode_workspace_bytes() bytes (KVQ_ERR_WORKSPACE otherwise).  With
- *                 kvq_decode_step_workspace_bytes() bytes, when the decode splits each
- *                 sequence over several workgroups and batch <= 512, a launch before the
- *                 decode builds its query operands (q' = q . T_K^-T as fp6 terms) once for
- *                 every (sequence, KV head), and the decode reads them instead of building
- *                 them in every workgroup; the output is the same bit for bit.
+ *                 kvq_decode_workspace_bytes() bytes (KVQ_ERR_WORKSPACE otherwise).
  * The written bytes equal those of kvq_quantize_append for the same new tokens. */
 kvq_status kvq_decode_step(const kvq_cache_desc* cache, const void* q, const void* k_new,
                            const void* v_new, kvq_dtype dtype, int32_t batch,

@@ -123,19 +123,13 @@ def test_decode_argument_checks(lib):
     # many sequences fill the GPU without splitting: no workspace
     assert lib.kvq_decode_workspace_bytes(C.byref(d), 64, 32, 16384) == 0
     assert lib.kvq_decode_workspace_bytes(C.byref(d), 1, 32, 0) == 0
-    # when the decode splits sequences, the step's workspace adds the query-operand image:
-    # 400 bytes per padded query head for every (sequence, KV head), after the partial
-    # outputs rounded up to 256 bytes
-    for (b, hq, msl) in ((1, 32, 16384), (1, 64, 16384), (16, 64, 131072), (3, 8, 5000)):
-        base = lib.kvq_decode_workspace_bytes(C.byref(d), b, hq, msl)
-        assert base > 0                                                           # split
-        gpad = 4 if hq // d.num_kv_heads <= 4 else (8 if hq // d.num_kv_heads <= 8 else 16)
-        want = (base + 255) // 256 * 256 + b * d.num_kv_heads * gpad * 400
-        assert lib.kvq_decode_step_workspace_bytes(C.byref(d), b, hq, msl) == want
-    # without a split (or past 512 sequences) there is no image: the decode's own size
-    for (b, hq, msl) in ((64, 32, 16384), (3, 8, 100), (600, 8, 200000)):
+    # the step's append runs in the decode's own launch: its workspace is the decode's, split
+    # or not
+    for (b, hq, msl) in ((1, 32, 16384), (1, 64, 16384), (16, 64, 131072), (3, 8, 5000),
+                         (64, 32, 16384), (3, 8, 100), (600, 8, 200000)):
         assert lib.kvq_decode_step_workspace_bytes(C.byref(d), b, hq, msl) == \
             lib.kvq_decode_workspace_bytes(C.byref(d), b, hq, msl)
+    assert lib.kvq_decode_workspace_bytes(C.byref(d), 1, 32, 16384) > 0          # split
     assert lib.kvq_decode_step_workspace_bytes(C.byref(d), 0, 32, 16) == 0
     assert lib.kvq_decode_step_workspace_bytes(C.byref(d), 1, 31, 16) == 0      # not a multiple of the KV heads
     assert lib.kvq_decode_step_workspace_bytes(None, 1, 32, 16) == 0

@@ -239,8 +239,7 @@ def test_qwen3_8b_b1_16k_full():
     assert row_rel_err(got, ref_g).max() <= TOL
     assert row_rel_err(got, ref).max() <= TOL
     # a decode step as the benchmark runs it: the new token rewrites the last position and
-    # takes part at full precision, and with the step's full workspace a launch before the
-    # decode builds the query operands that the 16 chunks read
+    # takes part at full precision; the append blocks ride in the 16-chunk decode launch
     rng_new = np.random.default_rng(12)
     kn = rng_new.standard_normal((1, H, 128)).astype(np.float32)
     vn = rng_new.standard_normal((1, H, 128)).astype(np.float32)
@@ -248,7 +247,7 @@ def test_qwen3_8b_b1_16k_full():
     vn = torch.from_numpy(vn).to(torch.bfloat16)
     new_slot = slots[n - 1:n].copy()
     need = api.decode_step_workspace_bytes(cache, 1, w.heads_q, n)
-    assert need > api.decode_workspace_bytes(cache, 1, w.heads_q, n)
+    assert need == api.decode_workspace_bytes(cache, 1, w.heads_q, n) > 0
     ws = torch.empty(need, dtype=torch.uint8, device="cuda")
     out = api.kvq_decode_step(cache, torch.from_numpy(q).to(torch.bfloat16).cuda(), kn.cuda(), vn.cuda(),
                               torch.from_numpy(new_slot).cuda(), torch.from_numpy(bt).cuda(),

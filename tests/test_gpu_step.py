@@ -1,6 +1,6 @@
 """GPU parity of the decode step (kvq_decode_step), through the C ABI: each sequence's new
 token takes part in the attention at full precision, and is encoded into the cache for later
-steps by an append running beside the decode.
+steps by append blocks in the decode's own launch.
 
   * The bytes the step writes equal those of kvq_quantize_append for the same new tokens
     (same encoder), and on the pages' other tokens nothing changes.
@@ -74,10 +74,10 @@ def _gpu(s, H, bits, quant, dtype, lens, fused=True, min_workspace=False):
     t = None if s["t"] is None else torch.from_numpy(s["t"]).to(tdt).cuda()
     tinv = None if s["tinv"] is None else torch.from_numpy(s["tinv"]).cuda()
     if fused and min_workspace:
-        # only the decode's partial outputs: the decode builds the query operands itself
+        # exactly the decode's partial outputs (a split decode needs them)
         need = api.decode_workspace_bytes(cache, len(lens), q.shape[1], max(lens))
-        ws = torch.empty(max(need, 1), dtype=torch.uint8, device="cuda")
-        assert need < api.decode_step_workspace_bytes(cache, len(lens), q.shape[1], max(lens))
+        assert need > 0 and need == api.decode_step_workspace_bytes(cache, len(lens), q.shape[1], max(lens))
+        ws = torch.empty(need, dtype=torch.uint8, device="cuda")
         out = api.kvq_decode_step(cache, q, kn, vn, sl, bt, seq, max(lens), t_k=t, t_k_inv_t=tinv, workspace=ws)
     elif fused:
         out = api.kvq_decode_step(cache, q, kn, vn, sl, bt, seq, max(lens), t_k=t, t_k_inv_t=tinv)
@@ -128,9 +128,9 @@ def test_step_writes_the_append_and_attends_at_full_precision(case):
         assert np.array_equal(kf, kp), describe_mismatch(kf, kp)
 
 
-# Shapes the decode splits over several workgroups per sequence: the step then builds the
-# query operands once, in a launch before its decode (cases 2 and 3 above, and these).
-IMAGE_CASES = [CASES[2], CASES[3],
+# Shapes the decode splits over several workgroups per sequence (cases 2 and 3 above, and
+# these): the append blocks ride in the split launch, and the chunks' partials are merged.
+SPLIT_CASES = [CASES[2], CASES[3],
     (2, 2, 4, [5000, 1300], (3, 3), ("percentile", "percentile"), "bf16", True),
     (1, 1, 16, [4200], (2, 4), ("rms", "percentile"), "f16", False),
     (3, 2, 1, [2049, 64, 1], (4, 2), ("percentile", "rms"), "f32", True),
@@ -138,21 +138,22 @@ IMAGE_CASES = [CASES[2], CASES[3],
 ]
 
 
-@pytest.mark.parametrize("case", range(len(IMAGE_CASES)))
-def test_step_query_operands_built_once(case):
-    """With the step's full workspace a launch before the decode builds its query operands
-    (q' = q T^-T as fp6 terms) and the decode reads them; with only the decode's workspace
-    the decode builds them itself.  Both run the same code: the outputs and the written
-    pages are identical bit for bit, and the output is within 2e-3 of the oracle's step."""
-    B, H, G, lens, bits, quant, dtype, transform = IMAGE_CASES[case]
+@pytest.mark.parametrize("case", range(len(SPLIT_CASES)))
+def test_split_step_with_a_caller_workspace(case):
+    """A split step given exactly the decode's workspace (kvq_decode_workspace_bytes) and one
+    that allocates its own: outputs and written pages identical bit for bit, the pages equal
+    to those kvq_quantize_append writes, and the output within 2e-3 of the oracle's step."""
+    B, H, G, lens, bits, quant, dtype, transform = SPLIT_CASES[case]
     rng = np.random.default_rng(100 + case)
     s = _setup(rng, B, H, G, lens, bits, quant, dtype, transform)
-    out_i, ki, vi = _gpu(s, H, bits, quant, dtype, lens, fused=True)
+    out_a, ka, va = _gpu(s, H, bits, quant, dtype, lens, fused=True)
     out_m, km, vm = _gpu(s, H, bits, quant, dtype, lens, fused=True, min_workspace=True)
-    assert np.array_equal(ki, km) and np.array_equal(vi, vm)
-    assert np.array_equal(out_i, out_m), np.abs(out_i - out_m).max()
-    ref = _oracle_step(s, lens, bits, ki, vi)
-    assert row_rel_err(out_i, ref).max() <= 2e-3
+    _, ks, vs = _gpu(s, H, bits, quant, dtype, lens, fused=False)
+    assert np.array_equal(ka, km) and np.array_equal(va, vm)
+    assert np.array_equal(ka, ks) and np.array_equal(va, vs)
+    assert np.array_equal(out_a, out_m), np.abs(out_a - out_m).max()
+    ref = _oracle_step(s, lens, bits, ka, va)
+    assert row_rel_err(out_a, ref).max() <= 2e-3
 
 
 # A sequence with a new token but no slot (slot < 0): the step still attends to its new
@@ -160,7 +161,7 @@ def test_step_query_operands_built_once(case):
 NO_SLOT_CASES = [
     (CASES[0], [1, 3]),           # one launch, the append in the decode's own launch
     (CASES[4], [0, 3, 4]),        # one launch, 4-bit, a 1- and a 2-token sequence without a slot
-    (CASES[2], [1]),              # split over chunks: the operand launch appends
+    (CASES[2], [1]),              # split over chunks
     (CASES[3], [0]),              # split, the only sequence without a slot: nothing is written
 ]
 
